@@ -1,0 +1,144 @@
+/*
+ * bitlinear.h — C ABI of the MI355X (gfx950) BitLinear library.
+ *
+ * The library computes the BitNet b1.58 BitLinear forward pass in five steps:
+ * absmean ternarisation of a weight matrix, packing of the codes, per-token
+ * symmetric absmax INT8 activation quantisation, an integer product of INT8
+ * activations against {-1, 0, +1} codes with INT32 accumulation, and the
+ * gamma * scale / 127 dequant epilogue. Sources, cited by page title and
+ * section:
+ *   [QAT-en] "QAT and BitNet: A Deep Dive into 1-bit and 1.58-bit
+ *            Quantization-Aware Training" (kongchang.com)
+ *   [QAT-zh] "QAT与BitNet：1-bit及1.58-bit量化训练解析" (kongchang.com)
+ *   [b158]   "BitNet b1.58深度解析：三值权重如何重塑大模型推理" (0539edu.com)
+ *
+ * Conventions for every call:
+ *  - Shapes: W is [N, K] row-major (out_features x in_features), x is [M, K]
+ *    row-major (M tokens), y is [M, N] row-major: y = x W^T ([b158] §4.2,
+ *    y_i = sum_j w_ij x_j).
+ *  - Every array argument is a DEVICE pointer, owned and allocated by the
+ *    caller, 16-byte aligned. The library never allocates, frees or
+ *    synchronises: each call only enqueues kernels on `stream` (a hipStream_t
+ *    passed as void*, NULL = the default stream) and returns.
+ *  - Argument errors are detected before any HIP call; the call then returns
+ *    BL_ERR_INVALID_ARG with no side effect. Bad arguments are: a NULL
+ *    required pointer, a pointer not 16-byte aligned, a negative size, K < 1,
+ *    K > 16909320 (127*K must fit in INT32), an unknown dtype / layout /
+ *    scheme, a too-small workspace. M = 0 or N = 0 is an empty problem and
+ *    returns BL_OK without launching anything (pack_weights needs N >= 1).
+ *  - If the current device is not a gfx950 GPU, or a launch fails, the call
+ *    returns BL_ERR_DEVICE (the HIP error is consumed). Kernels that fault
+ *    later surface at the caller's next synchronisation.
+ *  - Non-finite inputs (NaN, Inf) are outside the contract.
+ *  - Calls on different streams do not share state; the library holds no
+ *    mutable global state.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_INVALID_ARG = 1,
+    BL_ERR_UNSUPPORTED = 2,
+    BL_ERR_DEVICE = 3
+} bl_status;
+
+/* Element types of floating-point inputs and outputs. bf16 values are
+ * widened exactly to fp32 before any arithmetic. */
+typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
+
+/* Packed weight layouts ([b158] §2.3 and §6.3: two bits per weight with the
+ * patterns 00, 01, 10, four weights per byte; or five ternary values per
+ * byte since 3^5 = 243 <= 256, 1.6 bits per weight).
+ *
+ * BL_PACK_2BIT: the stored field is u = c + 1 (00 = -1, 01 = 0, 10 = +1; 11
+ *   is never written). A row takes row_bytes = roundup(ceil(K/4), 16) bytes.
+ *   Codes are grouped by 16 into one little-endian 32-bit word; code k of a
+ *   row sits in byte 4*(k/16) + (k%4) at bits 2*((k%16)/4)..+1, so that
+ *   (word >> 2j) & 0x03030303 holds codes 4j..4j+3 of the group in its four
+ *   bytes. Padding codes (k >= K) are 0.
+ * BL_PACK_BASE3: byte j of a row holds codes 5j..5j+4 as the base-3 number
+ *   t0 + 3 t1 + 9 t2 + 27 t3 + 81 t4 with t = c + 1 (first code in the least
+ *   significant trit; values 0..242). row_bytes = roundup(ceil(K/5), 16);
+ *   padding trits are t = 1 (code 0). */
+typedef enum { BL_PACK_2BIT = 0, BL_PACK_BASE3 = 1 } bl_layout;
+
+/* Weight quantisers.
+ * BL_TERNARY (b1.58): gamma = mean|W|; c = clamp(round(W / (gamma + eps)),
+ *   -1, 1), round half to even ([QAT-en] "The Ternary Weight Recipe" and its
+ *   ternary_weights code; [b158] §3.1).
+ * BL_BINARY (1-bit BitNet): alpha = mean(W); c = +1 where W > alpha, else -1;
+ *   the weight scale is beta = mean|W| ([QAT-en] "The BitLinear Recipe",
+ *   steps 2 and 4). */
+typedef enum { BL_TERNARY = 0, BL_BINARY = 1 } bl_scheme;
+
+/* Bytes one packed row of K codes occupies in `layout`; -1 for K < 1 or an
+ * unknown layout. Host-only, pure. */
+int64_t bitlinear_packed_row_bytes(int64_t K, int layout);
+
+/* Device workspace (bytes) bitlinear_pack_weights needs for an N x K matrix:
+ * it holds the per-block partial sums of the two-pass mean reduction. */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+
+/* Quantise and pack a latent weight matrix ([QAT-en] "The Ternary Weight
+ * Recipe"; [b158] §3.1 and §6.3; [QAT-en] "The BitLinear Recipe" for
+ * BL_BINARY).
+ *   W         [N, K] w_dtype (BL_F32 or BL_BF16), read only.
+ *   eps       added to gamma before the division (1e-5 in the pages' code);
+ *             ignored by BL_BINARY. Must be finite and >= 0.
+ *   packed    out: [N, bitlinear_packed_row_bytes(K, layout)] uint8.
+ *   gamma     out: 1 float, the weight scale the epilogue multiplies by
+ *             (gamma = mean|W| for BL_TERNARY; beta = mean|W| for BL_BINARY).
+ *             It stays on the device; no host synchronisation happens.
+ *   workspace device scratch of at least bitlinear_pack_workspace_bytes(N, K)
+ *             bytes; its contents are overwritten.
+ * The mean is accumulated in fp64 and rounded once to fp32. */
+bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K,
+                                 int scheme, int layout, float eps,
+                                 uint8_t *packed, float *gamma,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Per-token symmetric absmax INT8 quantisation ([b158] §3.2 and §5.2):
+ * s_m = max(max_k |x[m,k]|, 1e-6); xq = clamp(round(x / s_m * 127), -127, 127)
+ * with fp32 division, then * 127, then round half to even.
+ *   x      [M, K] x_dtype (BL_F32 or BL_BF16), read only.
+ *   xq     out: [M, K] int8 codes (never -128).
+ *   scale  out: [M] float, the s_m above. */
+bl_status bitlinear_quant_acts(const void *x, int x_dtype, int64_t M, int64_t K,
+                               int8_t *xq, float *scale, void *stream);
+
+/* Integer product and dequant epilogue ([b158] §4.2: +1 adds, -1 subtracts,
+ * 0 skips; §3.3: INT32 accumulator; §5.2-5.3: x_q / 127 * scale and
+ * out * gamma):
+ *   acc[m,n] = sum_k xq[m,k] * c[n,k]             (exact INT32)
+ *   y[m,n]   = acc[m,n] * gamma * scale[m] / 127  (fp32, then y_dtype)
+ *   xq, scale  from bitlinear_quant_acts ([M, K] int8, [M] float).
+ *   packed     [N, row_bytes] in `layout`; gamma: 1 float (device).
+ *   y          out: [M, N], y_dtype BL_F32 or BL_BF16 (round to nearest even).
+ *   acc        optional out: [M, N] int32 accumulators, or NULL.
+ * Dispatch on M: small batches (M <= 16) stream the packed weights once;
+ * larger M runs the tiled INT8 matrix-core product. */
+bl_status bitlinear_forward(const int8_t *xq, const float *scale,
+                            const uint8_t *packed, int layout, const float *gamma,
+                            int64_t M, int64_t N, int64_t K,
+                            void *y, int y_dtype, int32_t *acc, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *bitlinear_status_string(int status);
+
+/* Library version, (major << 16) | minor. */
+int bitlinear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

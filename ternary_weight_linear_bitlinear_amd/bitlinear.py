@@ -1,0 +1,168 @@
+"""Thin Python binding of ``libbitlinear.so`` (the C ABI in include/bitlinear.h).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the BitLinear pass runs in the library's HIP kernels.
+There is no CPU or PyTorch fallback: if the library is missing, importing
+this module raises.
+
+Functions keep the C names (``bitlinear_pack_weights``,
+``bitlinear_quant_acts``, ``bitlinear_forward``) and take torch tensors;
+``linear`` chains activation quantisation and the forward product.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitlinear.so")
+
+BL_OK, BL_ERR_INVALID_ARG, BL_ERR_UNSUPPORTED, BL_ERR_DEVICE = 0, 1, 2, 3
+BL_F32, BL_BF16 = 0, 1
+BL_PACK_2BIT, BL_PACK_BASE3 = 0, 1
+BL_TERNARY, BL_BINARY = 0, 1
+
+LAYOUTS = {"2bit": BL_PACK_2BIT, "base3": BL_PACK_BASE3}
+SCHEMES = {"ternary": BL_TERNARY, "binary": BL_BINARY}
+_DTYPES = {torch.float32: BL_F32, torch.bfloat16: BL_BF16}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m ternary_weight_linear_bitlinear_amd.build` "
+        "(there is no fallback path)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i64, _int, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_lib.bitlinear_packed_row_bytes.restype = _i64
+_lib.bitlinear_packed_row_bytes.argtypes = [_i64, _int]
+_lib.bitlinear_pack_workspace_bytes.restype = _sz
+_lib.bitlinear_pack_workspace_bytes.argtypes = [_i64, _i64]
+_lib.bitlinear_pack_weights.restype = _int
+_lib.bitlinear_pack_weights.argtypes = [_p, _int, _i64, _i64, _int, _int, _f32, _p, _p, _p, _sz, _p]
+_lib.bitlinear_quant_acts.restype = _int
+_lib.bitlinear_quant_acts.argtypes = [_p, _int, _i64, _i64, _p, _p, _p]
+_lib.bitlinear_forward.restype = _int
+_lib.bitlinear_forward.argtypes = [_p, _p, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
+_lib.bitlinear_status_string.restype = ctypes.c_char_p
+_lib.bitlinear_status_string.argtypes = [_int]
+_lib.bitlinear_version.restype = _int
+_lib.bitlinear_version.argtypes = []
+
+EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
+            "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
+            "bitlinear_status_string", "bitlinear_version"]
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.bitlinear_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != BL_OK:
+        raise BitLinearError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _layout(layout) -> int:
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+# ----------------------------------------------------------------------------
+def bitlinear_packed_row_bytes(K: int, layout="2bit") -> int:
+    return int(_lib.bitlinear_packed_row_bytes(K, _layout(layout)))
+
+
+def bitlinear_pack_workspace_bytes(N: int, K: int) -> int:
+    return int(_lib.bitlinear_pack_workspace_bytes(N, K))
+
+
+def bitlinear_version() -> int:
+    return int(_lib.bitlinear_version())
+
+
+def bitlinear_status_string(status: int) -> str:
+    return _lib.bitlinear_status_string(status).decode()
+
+
+def bitlinear_pack_weights(W: torch.Tensor, layout="2bit", scheme="ternary", eps: float = 1e-5,
+                           packed: torch.Tensor | None = None, gamma: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None):
+    """Quantise and pack W [N, K] (fp32 or bf16, on the GPU).
+
+    Returns (packed uint8 [N, row_bytes], gamma float32 [1]) on W's device."""
+    assert W.dim() == 2 and W.is_contiguous() and W.dtype in _DTYPES
+    N, K = W.shape
+    lay = _layout(layout)
+    rb = bitlinear_packed_row_bytes(K, lay)
+    dev = W.device
+    if packed is None:
+        packed = torch.empty((N, rb), dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+    wsb = bitlinear_pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(_lib.bitlinear_pack_weights(_ptr(W), _DTYPES[W.dtype], N, K,
+                                       SCHEMES[scheme] if isinstance(scheme, str) else int(scheme),
+                                       lay, float(eps), _ptr(packed), _ptr(gamma),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)),
+           "bitlinear_pack_weights")
+    return packed, gamma
+
+
+def bitlinear_quant_acts(x: torch.Tensor, xq: torch.Tensor | None = None,
+                         scale: torch.Tensor | None = None, stream=None):
+    """Per-token INT8 quantisation of x [M, K]; returns (xq int8 [M, K], scale f32 [M])."""
+    assert x.dim() == 2 and x.is_contiguous() and x.dtype in _DTYPES
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty(max(M, 1), dtype=torch.float32, device=x.device)[:M]
+    _check(_lib.bitlinear_quant_acts(_ptr(x), _DTYPES[x.dtype], M, K, _ptr(xq), _ptr(scale),
+                                     _stream(stream)), "bitlinear_quant_acts")
+    return xq, scale
+
+
+def bitlinear_forward(xq: torch.Tensor, scale: torch.Tensor, packed: torch.Tensor,
+                      gamma: torch.Tensor, N: int, K: int, layout="2bit",
+                      out_dtype=torch.float32, y: torch.Tensor | None = None,
+                      acc: torch.Tensor | bool | None = None, stream=None):
+    """y = (xq c^T) * gamma * scale / 127; returns y, or (y, acc) when acc is requested."""
+    M = xq.shape[0]
+    assert xq.dim() == 2 and xq.shape[1] == K and xq.dtype == torch.int8
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    want_acc = acc is not None and acc is not False
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _check(_lib.bitlinear_forward(_ptr(xq), _ptr(scale), _ptr(packed), _layout(layout),
+                                  _ptr(gamma), M, N, K, _ptr(y), _DTYPES[y.dtype],
+                                  _ptr(acc) if want_acc else None, _stream(stream)),
+           "bitlinear_forward")
+    return (y, acc) if want_acc else y
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int, layout="2bit",
+           out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """BitLinear forward of x [M, K] against packed weights: quantise, then multiply."""
+    xq, scale = bitlinear_quant_acts(x, stream=stream)
+    return bitlinear_forward(xq, scale, packed, gamma, N, x.shape[1], layout, out_dtype,
+                             stream=stream)

@@ -1,0 +1,136 @@
+// C ABI of the BitLinear library: argument validation, device check and
+// dispatch to the kernels. No allocation, no synchronisation; every call only
+// enqueues work on the caller's stream. The contract of each entry point is
+// documented in include/bitlinear.h.
+#include "../../include/bitlinear.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "bl_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxK = 2147483647LL / 127;  // 127 * K must fit in INT32
+constexpr int kMaxDevices = 64;
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch[kMaxDevices];
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int d) { return d == BL_F32 || d == BL_BF16; }
+bool valid_layout(int l) { return l == BL_PACK_2BIT || l == BL_PACK_BASE3; }
+bool valid_scheme(int s) { return s == BL_TERNARY || s == BL_BINARY; }
+
+bl_status device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return BL_ERR_DEVICE;
+    }
+    int st = g_arch[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return BL_ERR_DEVICE;
+        }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? BL_OK : BL_ERR_DEVICE;
+}
+
+bl_status launched(hipError_t e) {
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return BL_ERR_DEVICE;
+    }
+    return BL_OK;
+}
+
+int64_t row_bytes(int64_t K, int layout) {
+    return layout == BL_PACK_2BIT ? bl::row_bytes_2bit(K) : bl::row_bytes_base3(K);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bitlinear_packed_row_bytes(int64_t K, int layout) {
+    if (K < 1 || !valid_layout(layout)) return -1;
+    return row_bytes(K, layout);
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
+    if (N < 1 || K < 1) return 0;
+    return bl::pack_workspace_bytes(N * K);
+}
+
+bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K, int scheme,
+                                 int layout, float eps, uint8_t *packed, float *gamma,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (!W || !packed || !gamma || !workspace) return BL_ERR_INVALID_ARG;
+    if (!aligned16(W) || !aligned16(packed) || !aligned16(gamma) || !aligned16(workspace))
+        return BL_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || K > kMaxK) return BL_ERR_INVALID_ARG;
+    if (N > INT64_MAX / K) return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(w_dtype) || !valid_layout(layout) || !valid_scheme(scheme))
+        return BL_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f) return BL_ERR_INVALID_ARG;
+    if (workspace_bytes < bl::pack_workspace_bytes(N * K)) return BL_ERR_INVALID_ARG;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    return launched(bl::launch_pack(W, w_dtype, N, K, scheme, layout, eps, packed, gamma,
+                                    static_cast<double *>(workspace),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_quant_acts(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *xq,
+                               float *scale, void *stream) {
+    if (!x || !xq || !scale) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(scale)) return BL_ERR_INVALID_ARG;
+    if (M < 0 || K < 1 || K > kMaxK || M > 2147483647LL) return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype)) return BL_ERR_INVALID_ARG;
+    if (M == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    return launched(bl::launch_quant_acts(x, x_dtype, M, K, xq, scale,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_forward(const int8_t *xq, const float *scale, const uint8_t *packed,
+                            int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                            void *y, int y_dtype, int32_t *acc, void *stream) {
+    if (!xq || !scale || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(scale) || !aligned16(packed) || !aligned16(gamma) ||
+        !aligned16(y) || (acc && !aligned16(acc)))
+        return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || K > kMaxK) return BL_ERR_INVALID_ARG;
+    if (M > 65535LL * 128 || N > 2147483647LL) return BL_ERR_INVALID_ARG;
+    if (!valid_layout(layout) || !valid_dtype(y_dtype)) return BL_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M <= bl::kSkinnyMaxM)
+        return launched(
+            bl::launch_forward_skinny(xq, scale, packed, layout, gamma, M, N, K, y, y_dtype, acc, s));
+    return launched(
+        bl::launch_forward_gemm(xq, scale, packed, layout, gamma, M, N, K, y, y_dtype, acc, s));
+}
+
+const char *bitlinear_status_string(int status) {
+    switch (status) {
+        case BL_OK: return "ok";
+        case BL_ERR_INVALID_ARG: return "invalid argument";
+        case BL_ERR_UNSUPPORTED: return "unsupported";
+        case BL_ERR_DEVICE: return "device error (no gfx950 GPU, or a launch failed)";
+        default: return "unknown status";
+    }
+}
+
+int bitlinear_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

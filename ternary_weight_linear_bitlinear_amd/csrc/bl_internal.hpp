@@ -1,0 +1,50 @@
+// Internal declarations shared by the library's translation units (the
+// kernels and the C ABI). Nothing here is part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kLayout2Bit = 0;
+constexpr int kLayoutBase3 = 1;
+constexpr int kSchemeTernary = 0;
+constexpr int kSchemeBinary = 1;
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// Largest batch handled by the weight-streaming (decode) kernel.
+constexpr int64_t kSkinnyMaxM = 16;
+
+inline int64_t row_bytes_2bit(int64_t K) { return ((K + 3) / 4 + 15) / 16 * 16; }
+inline int64_t row_bytes_base3(int64_t K) { return ((K + 4) / 5 + 15) / 16 * 16; }
+
+// ---- weight quantisation (quant.hip) -------------------------------------
+// Number of partial sums the mean reduction writes for `count` elements.
+int absmean_parts(int64_t count);
+// Bytes of workspace: one (sum|w|, sum w) pair of doubles per part.
+size_t pack_workspace_bytes(int64_t count);
+hipError_t launch_pack(const void *W, int dtype, int64_t N, int64_t K, int scheme,
+                       int layout, float eps, uint8_t *packed, float *gamma,
+                       double *workspace, hipStream_t stream);
+hipError_t launch_quant_acts(const void *x, int dtype, int64_t M, int64_t K,
+                             int8_t *xq, float *scale, hipStream_t stream);
+
+// ---- products (skinny.hip, gemm.hip) -------------------------------------
+hipError_t launch_forward_skinny(const int8_t *xq, const float *scale,
+                                 const uint8_t *packed, int layout,
+                                 const float *gamma, int64_t M, int64_t N,
+                                 int64_t K, void *y, int y_dtype, int32_t *acc,
+                                 hipStream_t stream);
+hipError_t launch_forward_gemm(const int8_t *xq, const float *scale,
+                               const uint8_t *packed, int layout,
+                               const float *gamma, int64_t M, int64_t N,
+                               int64_t K, void *y, int y_dtype, int32_t *acc,
+                               hipStream_t stream);
+
+}  // namespace bl

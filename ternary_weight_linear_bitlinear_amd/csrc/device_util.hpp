@@ -1,0 +1,90 @@
+// Device helpers shared by the kernels: element loads, bf16 rounding, wave
+// reductions and the ternary code expansion used by the products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kPer16B = 4;
+    __device__ __forceinline__ static float get(const float *p, int64_t i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+    static constexpr int kPer16B = 8;
+    __device__ __forceinline__ static float get(const uint16_t *p, int64_t i) {
+        return bf16_bits_to_f32(p[i]);
+    }
+};
+
+// Load 8 consecutive elements starting at p (16-byte aligned for bf16,
+// 32-byte aligned for fp32) as floats.
+__device__ __forceinline__ void load8(const float *p, float v[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+// Wave-wide (64 lanes) reductions through cross-lane shuffles.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Expand one 32-bit word of the 2-bit layout (16 codes) into four dwords of
+// signed code bytes in natural order: dword j holds codes 4j..4j+3. The field
+// u = (word >> 2j) & 0x03030303 is mapped to c = u - 1 by a byte permute whose
+// table holds 0xFF, 0x00, 0x01 at selector values 0, 1, 2.
+__device__ __forceinline__ void expand_2bit_word(uint32_t w, int out[4]) {
+    constexpr uint32_t kTable = 0x000100FFu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t u = (w >> (2 * j)) & 0x03030303u;
+        out[j] = (int)__builtin_amdgcn_perm(0u, kTable, u);
+    }
+}
+
+// Base-3 decode table: entry v (0..242) holds the five signed codes t_i - 1
+// of v = sum t_i 3^i in bytes 0..4 (bytes 5..7 zero); entries 243..255 are
+// zero. Built once per workgroup into LDS from this arithmetic definition.
+__device__ __forceinline__ uint64_t base3_entry(uint32_t v) {
+    if (v >= 243u) return 0;
+    uint64_t e = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const uint32_t t = v % 3u;
+        v /= 3u;
+        e |= (uint64_t)(uint8_t)(int8_t)((int)t - 1) << (8 * i);
+    }
+    return e;
+}
+
+}  // namespace bl

@@ -1,0 +1,77 @@
+"""Comparison helpers for GPU-vs-oracle parity tests.
+
+Rules: weight codes, activation codes and INT32 accumulators are bit-exact,
+except at elements the oracle flags as lying within 1e-6 relative of a
+rounding boundary, which are excluded and counted; gamma and the activation
+scales agree within 1e-6 relative; fp32 outputs within 1e-5 relative; bf16
+outputs equal the round-to-nearest-even of the oracle's value, except where
+that value is within 1e-5 relative of a bf16 rounding midpoint (then either
+neighbour is accepted, and the element is counted).
+"""
+import numpy as np
+
+import oracle
+
+Y_RTOL = 1e-5
+SCALE_RTOL = 1e-6
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def check_codes(got_codes: np.ndarray, ref_codes: np.ndarray, flags: np.ndarray, what: str) -> int:
+    bad = got_codes != ref_codes
+    unflagged = bad & (flags == 0)
+    assert not unflagged.any(), (
+        f"{what}: {int(unflagged.sum())} unflagged mismatches, first at "
+        f"{np.argwhere(unflagged)[:5].tolist()}")
+    return int(bad.sum())
+
+
+def check_rel(got, ref, rtol, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    lim = rtol * np.abs(ref)
+    badm = err > lim
+    assert not badm.any(), (f"{what}: {int(badm.sum())} elements beyond rtol {rtol}; worst rel "
+                            f"{float(np.max(err / np.maximum(np.abs(ref), 1e-300)))}")
+
+
+def check_y_f32(y: np.ndarray, y64: np.ndarray, what="y"):
+    zero = y64 == 0
+    assert np.all(y[zero] == 0), f"{what}: zero accumulators must give exactly 0"
+    check_rel(y[~zero], y64[~zero], Y_RTOL, what)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_y_bf16(y_bits: np.ndarray, y64: np.ndarray, what="y_bf16") -> int:
+    """y_bits: uint16 bf16 patterns. Returns the number of midpoint-excluded elements."""
+    ref_bits = oracle.bf16_rne(y64.astype(np.float32))
+    neq = y_bits != ref_bits
+    if not neq.any():
+        return 0
+    # distance of the exact value to the nearest bf16 midpoint
+    ref = bf16_to_f64(ref_bits)
+    got = bf16_to_f64(y_bits)
+    lo = np.minimum(ref, got)
+    hi = np.maximum(ref, got)
+    mid = (lo + hi) / 2
+    near_mid = np.abs(y64 - mid) <= Y_RTOL * np.abs(y64)
+    # the two values must be adjacent bf16 numbers around a midpoint
+    adjacent = np.abs(y_bits.astype(np.int32) - ref_bits.astype(np.int32)) == 1
+    ok = near_mid & adjacent
+    assert np.all(ok[neq]), f"{what}: {int((neq & ~ok).sum())} bf16 outputs differ beyond the rule"
+    return int(neq.sum())
+
+
+def excluded_acc_mask(xq_bad: np.ndarray, code_bad: np.ndarray) -> np.ndarray:
+    """Outputs touched by a flagged (and mismatching) activation or weight code:
+    rows m with any xq mismatch, columns n with any code mismatch."""
+    rows = xq_bad.any(axis=1)
+    cols = code_bad.any(axis=1)
+    return rows[:, None] | cols[None, :]

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/bitlinear.h declares, computes the pure size helpers,
+and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+@pytest.fixture(scope="module")
+def bl():
+    from ternary_weight_linear_bitlinear_amd import bitlinear
+    return bitlinear
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported(bl):
+    names = declared_functions()
+    assert len(names) >= 7
+    lib = bl.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(bl.EXPORTED) == names
+
+
+def test_status_strings_and_version(bl):
+    assert bl.bitlinear_status_string(0) == "ok"
+    assert "invalid" in bl.bitlinear_status_string(1)
+    assert bl.bitlinear_version() >> 16 == 1
+
+
+def test_row_bytes(bl):
+    import oracle
+    for K in [1, 3, 4, 5, 16, 63, 64, 65, 79, 80, 81, 4096, 11008]:
+        assert bl.bitlinear_packed_row_bytes(K, "2bit") == oracle.row_bytes(K, "2bit")
+        assert bl.bitlinear_packed_row_bytes(K, "base3") == oracle.row_bytes(K, "base3")
+    assert bl.bitlinear_packed_row_bytes(0, "2bit") == -1
+    assert bl.bitlinear_packed_row_bytes(16, 7) == -1
+    assert bl.bitlinear_packed_row_bytes(4096, "2bit") == 1024
+    assert bl.bitlinear_packed_row_bytes(4096, "base3") == 832
+    assert bl.bitlinear_pack_workspace_bytes(0, 5) == 0
+    assert bl.bitlinear_pack_workspace_bytes(4096, 4096) % 16 == 0
+
+
+P = 0x10000  # a fake, 16-byte aligned address: never dereferenced on these paths
+
+
+def _pack(bl, **kw):
+    a = dict(W=P, dt=0, N=4, K=64, scheme=0, layout=0, eps=1e-5, packed=P, gamma=P, ws=P,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    return bl.library().bitlinear_pack_weights(a["W"], a["dt"], a["N"], a["K"], a["scheme"],
+                                                a["layout"], a["eps"], a["packed"], a["gamma"],
+                                                a["ws"], a["wsb"], a["stream"])
+
+
+def _quant(bl, **kw):
+    a = dict(x=P, dt=0, M=4, K=64, xq=P, scale=P, stream=None)
+    a.update(kw)
+    return bl.library().bitlinear_quant_acts(a["x"], a["dt"], a["M"], a["K"], a["xq"],
+                                              a["scale"], a["stream"])
+
+
+def _fwd(bl, **kw):
+    a = dict(xq=P, scale=P, packed=P, layout=0, gamma=P, M=4, N=8, K=64, y=P, ydt=0, acc=None,
+             stream=None)
+    a.update(kw)
+    return bl.library().bitlinear_forward(a["xq"], a["scale"], a["packed"], a["layout"],
+                                          a["gamma"], a["M"], a["N"], a["K"], a["y"], a["ydt"],
+                                          a["acc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(W=None), dict(packed=None), dict(gamma=None), dict(ws=None), dict(W=P + 4),
+    dict(packed=P + 8), dict(N=0), dict(N=-1), dict(K=0), dict(K=16909321), dict(dt=2),
+    dict(scheme=5), dict(layout=3), dict(eps=-1.0), dict(eps=float("nan")), dict(wsb=0),
+])
+def test_pack_rejects(bl, kw):
+    assert _pack(bl, **kw) == bl.BL_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(xq=None), dict(scale=None), dict(x=P + 2), dict(M=-1), dict(K=0),
+    dict(K=16909321), dict(dt=9),
+])
+def test_quant_rejects(bl, kw):
+    assert _quant(bl, **kw) == bl.BL_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(xq=None), dict(scale=None), dict(packed=None), dict(gamma=None), dict(y=None),
+    dict(y=P + 4), dict(acc=P + 4), dict(M=-1), dict(N=-1), dict(K=0), dict(K=16909321),
+    dict(layout=2), dict(ydt=3),
+])
+def test_forward_rejects(bl, kw):
+    assert _fwd(bl, **kw) == bl.BL_ERR_INVALID_ARG
+
+
+def test_empty_problems_are_noops(bl):
+    assert _quant(bl, M=0) == bl.BL_OK
+    assert _fwd(bl, M=0) == bl.BL_OK
+    assert _fwd(bl, N=0) == bl.BL_OK
+
+
+def test_no_device_reports_device_error(bl):
+    """Valid arguments with no gfx950 device visible: BL_ERR_DEVICE, nothing launched."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _pack(bl) == bl.BL_ERR_DEVICE
+    assert _quant(bl) == bl.BL_ERR_DEVICE
+    assert _fwd(bl) == bl.BL_ERR_DEVICE

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the CPU oracle
+on the same seeded inputs. Bars are stated in parity_util."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_linear_bitlinear_amd import synth
+from parity_util import (check_codes, check_rel, check_y_bf16, check_y_f32, excluded_acc_mask,
+                         to_np, SCALE_RTOL)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from ternary_weight_linear_bitlinear_amd import bitlinear
+    return bitlinear
+
+
+def dev(a: np.ndarray, bf16: bool = False) -> torch.Tensor:
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def y_bits(y: torch.Tensor) -> np.ndarray:
+    return to_np(y.view(torch.int16)).view(np.uint16)
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+PACK_CASES = [
+    (256, 256, "f32"), (37, 1000, "bf16"), (5, 17, "f32"), (3, 1, "f32"), (64, 80, "f32"),
+    (129, 4099, "bf16"), (1, 65, "bf16"),
+]
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
+@pytest.mark.parametrize("scheme", ["ternary", "binary"])
+@pytest.mark.parametrize("N,K,dtype", PACK_CASES)
+def test_pack_parity(bl, layout, scheme, N, K, dtype):
+    banner(f"pack {layout} {scheme} N={N} K={K} {dtype}")
+    p = synth.make_problem(M=1, N=N, K=K, seed=100 + N + K, dtype=dtype)
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, dtype == "bf16"), layout, scheme)
+    torch.cuda.synchronize()
+    if scheme == "ternary":
+        codes, flags, g_ref = oracle.ternary_codes(p.w)
+    else:
+        codes, flags, _alpha, g_ref = oracle.binary_codes(p.w)
+    g = to_np(gamma)[0]
+    check_rel([g], [g_ref], SCALE_RTOL, "gamma")
+    got = to_np(packed)
+    codes_gpu, bad = oracle.unpack(got, K, layout)
+    assert bad == 0
+    n_ex = check_codes(codes_gpu, codes, flags, "codes")
+    assert n_ex == 0 or g != g_ref
+    assert np.array_equal(oracle.pack(codes_gpu, layout), got), "layout/padding differs"
+
+
+def test_pack_deterministic(bl):
+    p = synth.make_problem(M=1, N=300, K=700, seed=7, dtype="bf16")
+    W = dev(p.w_store, True)
+    a, ga = bl.bitlinear_pack_weights(W, "2bit")
+    b, gb = bl.bitlinear_pack_weights(W, "2bit")
+    assert torch.equal(a, b) and torch.equal(ga, gb)
+
+
+def test_pack_zero_matrix(bl):
+    W = torch.zeros((16, 96), dtype=torch.float32, device="cuda")
+    packed, gamma = bl.bitlinear_pack_weights(W, "2bit")
+    assert to_np(gamma)[0] == 0.0
+    codes, bad = oracle.unpack(to_np(packed), 96, "2bit")
+    assert bad == 0 and not codes.any()
+
+
+# ----------------------------------------------------------------------------
+QUANT_CASES = [(8, 256, "f32", 0.0), (1, 4096, "bf16", 0.01), (3, 17, "f32", 0.0),
+               (5, 1000, "bf16", 0.0), (257, 64, "bf16", 0.0), (2, 20000, "f32", 0.0),
+               (4, 11008, "bf16", 0.01)]
+
+
+@pytest.mark.parametrize("M,K,dtype,outl", QUANT_CASES)
+def test_quant_acts_parity(bl, M, K, dtype, outl):
+    banner(f"quant M={M} K={K} {dtype}")
+    p = synth.make_problem(M=M, N=1, K=K, seed=200 + M + K, dtype=dtype, outlier_frac=outl)
+    x_store = p.x_store.copy()
+    x_ref = p.x.copy()
+    if M >= 3:  # one all-zero token
+        x_store[1] = 0
+        x_ref[1] = 0.0
+    xq, scale = bl.bitlinear_quant_acts(dev(x_store, dtype == "bf16"))
+    torch.cuda.synchronize()
+    xq_ref, s_ref, flags = oracle.quant_acts(x_ref)
+    check_rel(to_np(scale), s_ref, SCALE_RTOL, "scale")
+    assert np.array_equal(to_np(scale), s_ref)  # a max is exact
+    n_ex = check_codes(to_np(xq), xq_ref, flags, "xq")
+    assert n_ex == 0, "same fp32 steps on both sides: no boundary mismatch expected"
+
+
+# ----------------------------------------------------------------------------
+FWD_CASES = [
+    (1, 256, 256), (1, 31, 100), (2, 300, 1000), (3, 64, 64), (5, 16, 1), (8, 256, 256),
+    (16, 100, 4096), (16, 33, 17), (17, 256, 256), (64, 130, 1000), (130, 300, 260),
+    (257, 257, 320), (33, 1, 160), (128, 128, 4096), (300, 512, 129),
+]
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
+@pytest.mark.parametrize("M,N,K", FWD_CASES)
+def test_forward_stage_parity(bl, layout, M, N, K):
+    """Both sides get the same codes, activations, scales and gamma: the INT32
+    accumulators must be bit-exact and y within the output tolerance."""
+    banner(f"forward {layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    scale = rng.uniform(0.5, 30.0, size=M).astype(np.float32)
+    gamma = np.float32(0.0161)
+    packed = oracle.pack(codes, layout)
+    g = torch.tensor([gamma, 0, 0, 0], dtype=torch.float32, device="cuda")
+    for ydt in (torch.float32, torch.bfloat16):
+        y, acc = bl.bitlinear_forward(dev(xq), dev(scale), dev(packed), g, N, K, layout, ydt,
+                                      acc=True)
+        torch.cuda.synchronize()
+        acc_ref = oracle.int_product(xq, codes)
+        assert np.array_equal(to_np(acc), acc_ref), "INT32 accumulators differ"
+        y64 = oracle.epilogue(acc_ref, gamma, scale)
+        if ydt == torch.float32:
+            check_y_f32(to_np(y), y64)
+        else:
+            check_y_bf16(y_bits(y), y64)
+
+
+# ----------------------------------------------------------------------------
+def run_gpu_pipeline(bl, p, layout, scheme="ternary", out_dtype=torch.float32):
+    bf = p.dtype == "bf16"
+    W = dev(p.w_store, bf)
+    x = dev(p.x_store, bf)
+    packed, gamma = bl.bitlinear_pack_weights(W, layout, scheme)
+    xq, scale = bl.bitlinear_quant_acts(x)
+    y, acc = bl.bitlinear_forward(xq, scale, packed, gamma, p.N, p.K, layout, out_dtype,
+                                  acc=True)
+    torch.cuda.synchronize()
+    return dict(packed=to_np(packed), gamma=to_np(gamma)[0], xq=to_np(xq), scale=to_np(scale),
+                acc=to_np(acc), y=y)
+
+
+def check_end_to_end(got, ref, p, layout, out_dtype):
+    check_rel([got["gamma"]], [ref["gamma"]], SCALE_RTOL, "gamma")
+    codes_gpu, bad = oracle.unpack(got["packed"], p.K, layout)
+    assert bad == 0
+    code_bad = codes_gpu != ref["codes"]
+    check_codes(codes_gpu, ref["codes"], ref["wflags"], "codes")
+    xq_bad = got["xq"] != ref["xq"]
+    check_codes(got["xq"], ref["xq"], ref["xflags"], "xq")
+    assert np.array_equal(got["scale"], ref["scale"])
+    ex = excluded_acc_mask(xq_bad, code_bad)
+    assert np.array_equal(got["acc"][~ex], ref["acc"][~ex])
+    keep = ~ex
+    y = got["y"]
+    if out_dtype == torch.float32:
+        check_y_f32(to_np(y)[keep], ref["y64"][keep])
+    else:
+        check_y_bf16(y_bits(y)[keep], ref["y64"][keep])
+    return int(ex.sum())
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
+@pytest.mark.parametrize("scheme", ["ternary", "binary"])
+def test_end_to_end_tiny(bl, layout, scheme):
+    """M=8, K=256, N=256, fp32 inputs and output (the oracle's small workload)."""
+    banner(f"e2e tiny {layout} {scheme}")
+    p = synth.workload("tiny")
+    got = run_gpu_pipeline(bl, p, layout, scheme)
+    ref = oracle.forward(p.w, p.x, layout, scheme)
+    assert check_end_to_end(got, ref, p, layout, torch.float32) == 0
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
+def test_end_to_end_decode_full(bl, layout):
+    """Decode GEMV at full size: M=1, 4096 x 4096, bf16 inputs with outliers."""
+    banner(f"e2e decode {layout}")
+    p = synth.workload("decode")
+    got = run_gpu_pipeline(bl, p, layout)
+    ref = oracle.forward(p.w, p.x, layout)
+    assert check_end_to_end(got, ref, p, layout, torch.float32) == 0
+
+
+@pytest.mark.parametrize("M", [16, 512])
+def test_end_to_end_block_layer(bl, M):
+    """The FFN down projection (K = 11008) at decode batch 16 and prefill 512."""
+    banner(f"e2e block down M={M}")
+    p = synth.block_layer(5, M)
+    got = run_gpu_pipeline(bl, p, "2bit", out_dtype=torch.bfloat16)
+    ref = oracle.forward(p.w, p.x, "2bit")
+    check_end_to_end(got, ref, p, "2bit", torch.bfloat16)
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
+def test_prefill_full_size_sampled(bl, layout):
+    """Prefill at full size (M=2048, K=4096, N=11008, bf16 out): gamma, every
+    code and every activation code are compared; accumulators and outputs on
+    a sample of 24 token rows (all 11008 columns)."""
+    banner(f"prefill full {layout}")
+    p = synth.workload("prefill")
+    got = run_gpu_pipeline(bl, p, layout, out_dtype=torch.bfloat16)
+    codes, wflags, g_ref = oracle.ternary_codes(p.w)
+    check_rel([got["gamma"]], [g_ref], SCALE_RTOL, "gamma")
+    codes_gpu, bad = oracle.unpack(got["packed"], p.K, layout)
+    assert bad == 0
+    check_codes(codes_gpu, codes, wflags, "codes")
+    xq_ref, s_ref, xflags = oracle.quant_acts(p.x)
+    check_codes(got["xq"], xq_ref, xflags, "xq")
+    assert np.array_equal(got["scale"], s_ref)
+    rows = np.random.default_rng(0).choice(p.M, 24, replace=False)
+    rows = np.concatenate([rows, [0, p.M - 1]])
+    acc_ref = oracle.int_product(xq_ref[rows], codes)
+    code_bad = codes_gpu != codes
+    cols_ok = ~code_bad.any(axis=1)
+    assert np.array_equal(got["acc"][rows][:, cols_ok], acc_ref[:, cols_ok])
+    y64 = oracle.epilogue(acc_ref, g_ref, s_ref[rows])
+    check_y_bf16(y_bits(got["y"])[rows][:, cols_ok], y64[:, cols_ok])
+
+
+def test_zero_activation_row_gives_zero_output(bl):
+    p = synth.make_problem(M=20, N=64, K=256, seed=3, dtype="f32")
+    p.x_store[4] = 0.0
+    got = run_gpu_pipeline(bl, p, "2bit")
+    assert got["scale"][4] == np.float32(1e-6)
+    assert not got["xq"][4].any() and not got["acc"][4].any()
+    assert torch.all(got["y"][4] == 0)
