@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitLinear hot path on one MI355X.
+
+Headline (the JSON line's `value`): decode GEMV weight throughput, GB/s of
+packed 2-bit weights streamed per second, on the decode workload (M = 1
+token, W 4096 x 4096 bf16 quantised once, x bf16 N(0,1) with 1% outliers at
++/-20). One step = one token through one layer: per-token INT8 quantisation
+of x, then the integer product with the fused dequant epilogue. Steps rotate
+over 128 distinct packed weight copies (512 MiB, twice the 256 MB
+Infinity Cache) so the weights come from HBM.
+
+The same run measures the other rows of the path and reports them under
+"rows": the base-3 layout of the decode GEMV, weight packing, activation
+quantisation at prefill size, the prefill GEMM (M = 2048, K = 4096,
+N = 11008, INT8 TOPS) and one transformer block's six BitLinear layers at
+decode batch 16 and prefill 512 (tokens/s).
+
+Timing: every measured sequence is captured once into a HIP graph and
+replayed between two HIP events on the replay stream, so host-side launch
+cost is not measured. `roofline` describes the dominant kernel (the 2-bit
+decode GEMV): algorithmic bytes per launch over its mean launch duration,
+from a graph of 256 back-to-back launches over rotating weight copies. `cpu_baseline` times the CPU oracle on
+a bounded sample of the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5033.0        # dense INT8 MFMA: 256 CU x 4 SIMD x 2048 ops/clk x 2.4 GHz
+METRIC = "BitLinear weight GB/s (decode GEMV) + INT8 TOPS (prefill), % of roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=128, help="distinct packed weight copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", default="", help="comma list of rows to run (profiling runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described, not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ternary_weight_linear_bitlinear_amd import build as _build
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build_library()
+    from ternary_weight_linear_bitlinear_amd import bitlinear as bl
+    from ternary_weight_linear_bitlinear_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    only = set(filter(None, args.only.split(",")))
+
+    def want(name):
+        return not only or name in only
+
+    def to_dev(a, bf16):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    def graph_ms(fn, n, warm=1):
+        """Capture fn(0..n-1) into one HIP graph; replay it `warm` times untimed,
+        then once between two HIP events on the replay stream. Returns ms per call."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)  # first call outside capture (sets kernel attributes)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        for _ in range(warm):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / n
+
+    rows = {}
+
+    # ---------------------------------------------------------------- decode
+    log("decode workload: generating inputs")
+    p = synth.workload("decode")
+    W = to_dev(p.w_store, True)
+    R = args.copies
+    xs = [to_dev(synth.make_problem(M=1, N=1, K=p.K, seed=1000 + r, dtype="bf16",
+                                    outlier_frac=0.01).x_store, True) for r in range(R)]
+    decode = {}
+    for layout in ("2bit", "base3"):
+        packed, gamma = bl.bitlinear_pack_weights(W, layout)
+        copies = [packed.clone() for _ in range(R)]
+        y = torch.empty((1, p.N), dtype=torch.float32, device=dev)
+        xq = torch.empty((1, p.K), dtype=torch.int8, device=dev)
+        sc = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+        xq_r, sc_r = [], []
+        for r in range(R):
+            a, b = bl.bitlinear_quant_acts(xs[r])
+            xq_r.append(a)
+            sc_r.append(b)
+        rb = packed.shape[1]
+        wbytes = p.N * rb
+
+        def step(i, copies=copies, gamma=gamma, layout=layout, y=y, xq=xq, sc=sc):
+            r = i % R
+            bl.bitlinear_quant_acts(xs[r], xq=xq, scale=sc)
+            bl.bitlinear_forward(xq, sc, copies[r], gamma, p.N, p.K, layout, y=y)
+
+        def gemv(i, copies=copies, gamma=gamma, layout=layout, y=y):
+            r = i % R
+            bl.bitlinear_forward(xq_r[r], sc_r[r], copies[r], gamma, p.N, p.K, layout, y=y)
+
+        for i in range(args.warmup):
+            step(i)
+        # the timed region is one graph replay of exactly `steps` steps
+        ms_step = graph_ms(step, args.steps)
+        k_mean = graph_ms(gemv, 2 * R)
+        alg = wbytes + p.K + 4 + 4 + 4 * p.N
+        decode[layout] = dict(ms_per_step=ms_step, weight_bytes=wbytes,
+                              weight_gbs=wbytes / (ms_step * 1e-3) / 1e9,
+                              gemv_ms_mean=k_mean,
+                              gemv_alg_bytes=alg,
+                              gemv_gbs=alg / (k_mean * 1e-3) / 1e9)
+        log(f"decode {layout}: step {ms_step*1e3:.2f} us, gemv {k_mean*1e3:.2f} us "
+            f"({decode[layout]['gemv_gbs']:.0f} GB/s)")
+        del copies
+        torch.cuda.empty_cache()
+    rows["decode_gemv"] = decode
+
+    # ------------------------------------------------------------------ pack
+    if want("pack"):
+        ws = torch.empty(bl.bitlinear_pack_workspace_bytes(p.N, p.K), dtype=torch.uint8, device=dev)
+        pk = {}
+        for layout in ("2bit", "base3"):
+            packed = torch.empty((p.N, bl.bitlinear_packed_row_bytes(p.K, layout)),
+                                 dtype=torch.uint8, device=dev)
+            g = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+            f = lambda i, layout=layout, packed=packed, g=g: bl.bitlinear_pack_weights(
+                W, layout, packed=packed, gamma=g, workspace=ws)
+            ms = graph_ms(f, 20)
+            byt = 2 * p.N * p.K * 2 + packed.numel()  # W read by both passes + codes written
+            pk[layout] = dict(ms=ms, gbs=byt / (ms * 1e-3) / 1e9)
+            log(f"pack {layout}: {ms*1e3:.1f} us")
+        rows["pack_decode_weights"] = pk
+
+    # ------------------------------------------------------------- prefill
+    if want("prefill"):
+        log("prefill workload: generating inputs")
+        q = synth.workload("prefill")
+        Wp = to_dev(q.w_store, True)
+        xp = to_dev(q.x_store, True)
+        xq, sc = bl.bitlinear_quant_acts(xp)
+        qa_ms = graph_ms(lambda i: bl.bitlinear_quant_acts(xp, xq=xq, scale=sc), 20)
+        pre = {"quant_acts_ms": qa_ms,
+               "quant_acts_gbs": (q.M * q.K * 3 + 4 * q.M) / (qa_ms * 1e-3) / 1e9}
+        ops = 2.0 * q.M * q.N * q.K
+        for layout in ("2bit", "base3"):
+            packed, gamma = bl.bitlinear_pack_weights(Wp, layout)
+            y = torch.empty((q.M, q.N), dtype=torch.bfloat16, device=dev)
+            f = lambda i, packed=packed, gamma=gamma, layout=layout, y=y: bl.bitlinear_forward(
+                xq, sc, packed, gamma, q.N, q.K, layout, torch.bfloat16, y=y)
+            ms = graph_ms(f, 10)
+            pre[layout] = dict(gemm_ms=ms, tops=ops / (ms * 1e-3) / 1e12,
+                               frac=ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS)
+            log(f"prefill {layout}: {ms*1e3:.1f} us = {pre[layout]['tops']:.0f} TOPS")
+        rows["prefill_gemm"] = pre
+        del Wp, xp, xq, sc
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------- block stack
+    if want("block"):
+        log("block stack: generating inputs")
+        layers = []
+        for i, (name, N, K) in enumerate(synth.BLOCK_LAYERS):
+            pb = synth.block_layer(i, 1)
+            packed, gamma = bl.bitlinear_pack_weights(to_dev(pb.w_store, True), "2bit")
+            layers.append((name, N, K, packed, gamma))
+        blk = {}
+        for M in (16, 512):
+            ncopy = 16 if M == 16 else 1
+            cps = [[(n, N, K, pk.clone() if c else pk, g) for (n, N, K, pk, g) in layers]
+                   for c in range(ncopy)]
+            xin = {K: to_dev(synth.make_problem(M=M, N=1, K=K, seed=77 + K, dtype="bf16").x_store, True)
+                   for K in (4096, 11008)}
+            ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for (_, N, _, _, _) in layers]
+            qbuf = {K: (torch.empty((M, K), dtype=torch.int8, device=dev),
+                        torch.empty(M, dtype=torch.float32, device=dev)) for K in (4096, 11008)}
+
+            def block(i, cps=cps, xin=xin, ys=ys, qbuf=qbuf):
+                # Q, K, V share one quantised input; O, up and down each quantise their own
+                ls = cps[i % len(cps)]
+                for j, (_, N, K, pk, g) in enumerate(ls):
+                    if j in (0, 3, 4, 5):
+                        bl.bitlinear_quant_acts(xin[K], xq=qbuf[K][0], scale=qbuf[K][1])
+                    bl.bitlinear_forward(qbuf[K][0], qbuf[K][1], pk, g, N, K, "2bit",
+                                         torch.bfloat16, y=ys[j])
+
+            ms = graph_ms(block, 32 if M == 16 else 8)
+            blk[f"M{M}"] = dict(ms_per_block=ms, tokens_per_s=M / (ms * 1e-3))
+            log(f"block M={M}: {ms*1e3:.1f} us/block, {M/(ms*1e-3):.3g} tok/s")
+            del cps
+            torch.cuda.empty_cache()
+        rows["block_stack"] = blk
+
+    # --------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        codes, _, gamma = oracle.ternary_codes(p.w)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            xq_, s_, _ = oracle.quant_acts(p.x)
+            acc_ = oracle.int_product(xq_, codes)
+            oracle.epilogue(acc_, gamma, s_)
+            n += 1
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        wb = decode["2bit"]["weight_bytes"]
+        cpu = {"value": wb * n / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{n} decode steps (quant_acts + int64 product + fp64 epilogue, M=1, "
+                         f"K=N=4096) in {dt:.1f} s; value = 2-bit weight bytes per step / time",
+               "host_cpus": os.cpu_count()}
+        log(f"cpu baseline: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    # ------------------------------------------------------------ roofline
+    d2 = decode["2bit"]
+    roof = {"kernel": "skinny_kernel<2bit> (decode GEMV, M=1, 4096x4096)", "bound": "hbm",
+            "achieved": d2["gemv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": d2["gemv_gbs"] / HBM_PEAK_GBS, "traffic": None,
+            "alg_bytes_per_launch": d2["gemv_alg_bytes"],
+            "launch_ms_mean": d2["gemv_ms_mean"]}
+    counters = os.path.join(ROOT, "profiles", "gemv_2bit_decode_counters.json")
+    if os.path.exists(counters):
+        with open(counters) as f:
+            c = json.load(f)
+        src = os.path.join(ROOT, "ternary_weight_linear_bitlinear_amd", "csrc", "skinny.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if c.get("source_sha") == sha:
+            roof["traffic"] = c.get("hbm_bytes_per_launch")
+
+    ms = d2["ms_per_step"]
+    line = {
+        "metric": METRIC, "value": d2["weight_gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV: M=1 token, W 4096x4096 bf16 ~N(0,0.02) quantised "
+                               "once (absmean ternary, 2-bit packed), x bf16 ~N(0,1) + 1% +/-20 "
+                               "outliers; step = quant_acts + forward; 128 rotating weight copies",
+                   "M": 1, "K": 4096, "N": 4096, "layout": "2bit", "out": "fp32"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

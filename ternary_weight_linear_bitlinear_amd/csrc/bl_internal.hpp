@@ -21,6 +21,18 @@ constexpr int kBF16 = 1;
 // Largest batch handled by the weight-streaming (decode) kernel.
 constexpr int64_t kSkinnyMaxM = 16;
 
+// Kernels using more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
+// must raise their limit once. `done` is a flag owned by the caller, one per
+// kernel; setting the attribute twice is harmless, so a race is benign.
+template <typename F>
+hipError_t allow_dynamic_lds(F *kernel, size_t bytes, int *done) {
+    if (bytes <= 65536 || *done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess) *done = 1;
+    return e;
+}
+
 inline int64_t row_bytes_2bit(int64_t K) { return ((K + 3) / 4 + 15) / 16 * 16; }
 inline int64_t row_bytes_base3(int64_t K) { return ((K + 4) / 5 + 15) / 16 * 16; }
 

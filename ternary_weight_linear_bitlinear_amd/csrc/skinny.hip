@@ -7,121 +7,149 @@
 // ([b158] §3.3), then scaled by gamma * scale[m] / 127 ([b158] §5.2-5.3).
 //
 // Work split: a block owns 16 consecutive weight rows; its KS waves split the
-// row length K and their 16x16 partial tiles are added through LDS. In one
-// "super-step" the four 16-lane groups of a wave each take one 16-byte unit
-// of packed codes per row (64 codes in the 2-bit layout, 80 in base-3); the
-// matrix-core k slots of lane group g are mapped to that unit's codes, and
-// the activation operand is loaded with the same mapping, so the sum over
-// the 64 k slots of one instruction is a sum over real codes only.
+// row length K. One "super-step" of a wave covers four 16-byte units of
+// packed codes per row (64 codes per unit in the 2-bit layout, 80 in base-3),
+// one unit per 16-lane group; the matrix-core k slots of lane group g are
+// mapped to that unit's codes and the activation operand is read with the
+// same mapping, so every instruction sums over real codes only. A wave
+// issues the loads of all NSS super-steps of a round before consuming any,
+// so each lane keeps NSS 16-byte weight loads in flight, while the block
+// stages the round's slice of the activations in LDS. The KS partial 16x16
+// tiles are added through LDS.
 #include "bl_internal.hpp"
 #include "device_util.hpp"
 
 namespace bl {
 namespace {
 
-// Load 16 activation bytes xq[t, k .. k+15], zero past K.
-__device__ __forceinline__ v4i load_act16(const int8_t *__restrict__ row, int64_t K,
-                                          int64_t k, bool aligned) {
-    v4i r = {0, 0, 0, 0};
-    if (k + 16 <= K && aligned) {
-        r = *reinterpret_cast<const v4i *>(row + k);
-    } else if (k < K) {
-        uint32_t d[4] = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < 16; ++e)
-            if (k + e < K) d[e / 4] |= (uint32_t)(uint8_t)row[k + e] << (8 * (e % 4));
-        r = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+template <int LAYOUT>
+struct SkinnyCfg {
+    static constexpr int kUnitCodes = LAYOUT == kLayout2Bit ? 64 : 80;
+    static constexpr int kSteps = kUnitCodes / 16;  // MFMA instructions per unit
+};
+
+// Decode one 16-byte unit into signed code bytes (natural k order).
+template <int LAYOUT>
+__device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut, int c[20]) {
+    if (LAYOUT == kLayout2Bit) {
+        expand_2bit_word(wv.x, c + 0);
+        expand_2bit_word(wv.y, c + 4);
+        expand_2bit_word(wv.z, c + 8);
+        expand_2bit_word(wv.w, c + 12);
+    } else {
+        uint32_t d[20];
+#pragma unroll
+        for (int i = 0; i < 20; ++i) d[i] = 0u;
+        const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t v = (w[j / 4] >> (8 * (j % 4))) & 0xFFu;
+            const uint64_t e = lut[(j % 4) * 256 + v];
+            const int dw = (5 * j) / 4;
+            d[dw] |= (uint32_t)e;
+            d[dw + 1] |= (uint32_t)(e >> 32);
+        }
+#pragma unroll
+        for (int i = 0; i < 20; ++i) c[i] = (int)d[i];
     }
-    return r;
 }
 
-template <int LAYOUT, int KS, typename YT>
+template <int LAYOUT, int KS, int NSS, typename YT>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ scale,
     const uint8_t *__restrict__ packed, const float *__restrict__ gamma_p, int M, int64_t N,
     int64_t K, int64_t rb, YT *__restrict__ y, int32_t *__restrict__ acc_out) {
-    constexpr int kUnitCodes = LAYOUT == kLayout2Bit ? 64 : 80;
-    constexpr int kSteps = kUnitCodes / 16;  // MFMA instructions per unit
-    __shared__ uint64_t lut[LAYOUT == kLayoutBase3 ? 4 * 256 : 1];
-    __shared__ v4i part[KS][64];
+    using C = SkinnyCfg<LAYOUT>;
+    constexpr int kRoundUnits = KS * NSS * 4;                 // units per round
+    constexpr int kRoundK = kRoundUnits * C::kUnitCodes;       // codes per round
+    constexpr int kActStride = kRoundK + 16;                   // LDS row stride (bytes)
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint64_t *lut = reinterpret_cast<uint64_t *>(smem);                 // base-3 only
+    int8_t *act = reinterpret_cast<int8_t *>(smem + (LAYOUT == kLayoutBase3 ? 8192 : 0));
+    v4i *part = reinterpret_cast<v4i *>(smem + (LAYOUT == kLayoutBase3 ? 8192 : 0));
 
     const int wave = threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
-    const int r = lane % 16;  // weight row within the block / token index
+    const int r = lane % 16;  // weight row within the block (A) / token (B)
     const int g = lane / 16;  // lane group = unit within the super-step
     const int64_t n0 = (int64_t)blockIdx.x * 16;
 
     if (LAYOUT == kLayoutBase3) {
-        // four copies of the decode table, shifted by 0..3 bytes
-        for (int i = threadIdx.x; i < 4 * 256; i += 64 * KS) {
-            const int a = i / 256, v = i % 256;
-            lut[i] = base3_entry((uint32_t)v) << (8 * a);
-        }
-        __syncthreads();
+        for (int i = threadIdx.x; i < 4 * 256; i += 64 * KS)
+            lut[i] = base3_entry((uint32_t)(i % 256)) << (8 * (i / 256));
     }
 
     const int64_t units = rb / 16;
-    const int64_t supers = (units + 3) / 4;
     const bool row_ok = n0 + r < N;
     const uint8_t *wrow = packed + (n0 + r) * rb;
-    const bool tok_ok = r < M;
-    const int8_t *xrow = xq + (int64_t)r * K;
     const bool aligned = (K % 16) == 0;
 
     v4i acc = {0, 0, 0, 0};
-    for (int64_t ss = wave; ss < supers; ss += KS) {
-        const int64_t unit = ss * 4 + g;
-        const bool unit_ok = unit < units;
-        uint4 wv = make_uint4(0u, 0u, 0u, 0u);
-        if (unit_ok && row_ok) wv = *reinterpret_cast<const uint4 *>(wrow + unit * 16);
-        int c[kSteps * 4];
-        if (LAYOUT == kLayout2Bit) {
-            expand_2bit_word(wv.x, c + 0);
-            expand_2bit_word(wv.y, c + 4);
-            expand_2bit_word(wv.z, c + 8);
-            expand_2bit_word(wv.w, c + 12);
-        } else {
-            uint32_t d[20];
+    for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
+        // 1. issue every weight load of this round
+        uint4 wv[NSS];
 #pragma unroll
-            for (int i = 0; i < 20; ++i) d[i] = 0u;
-            const uint32_t bytes[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t v = (bytes[j / 4] >> (8 * (j % 4))) & 0xFFu;
-                const uint64_t e = lut[(j % 4) * 256 + v];
-                const int dw = (5 * j) / 4;
-                d[dw] |= (uint32_t)e;
-                d[dw + 1] |= (uint32_t)(e >> 32);
-            }
-#pragma unroll
-            for (int i = 0; i < 20; ++i) c[i] = (int)d[i];
+        for (int s = 0; s < NSS; ++s) {
+            const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
+            wv[s] = make_uint4(0u, 0u, 0u, 0u);
+            if (row_ok && unit < units) wv[s] = *reinterpret_cast<const uint4 *>(wrow + unit * 16);
         }
-        const int64_t kbase = unit * kUnitCodes;
+        // 2. stage activations xq[0:M, k0 : k0 + kRoundK] in LDS (zero past K)
+        const int64_t k0 = u0 * C::kUnitCodes;
+        __syncthreads();  // previous round's readers are done
+        const int chunks = M * (kRoundK / 16);
+        for (int q = threadIdx.x; q < chunks; q += 64 * KS) {
+            const int t = q / (kRoundK / 16), cc = q % (kRoundK / 16);
+            const int64_t k = k0 + cc * 16;
+            const int8_t *src = xq + (int64_t)t * K;
+            v4i v = {0, 0, 0, 0};
+            if (aligned && k + 16 <= K) {
+                v = *reinterpret_cast<const v4i *>(src + k);
+            } else if (k < K) {
+                uint32_t d[4] = {0u, 0u, 0u, 0u};
+                for (int e = 0; e < 16; ++e)
+                    if (k + e < K) d[e / 4] |= (uint32_t)(uint8_t)src[k + e] << (8 * (e % 4));
+                v = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+            }
+            *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) = v;
+        }
+        __syncthreads();
+        // 3. expand and multiply
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            v4i b = {0, 0, 0, 0};
-            if (tok_ok && unit_ok) b = load_act16(xrow, K, kbase + 16 * s, aligned);
-            const v4i a = {c[4 * s], c[4 * s + 1], c[4 * s + 2], c[4 * s + 3]};
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+        for (int s = 0; s < NSS; ++s) {
+            int c[20];
+            decode_unit<LAYOUT>(wv[s], lut, c);
+            const int ul = (s * KS + wave) * 4 + g;  // unit within the round
+#pragma unroll
+            for (int st = 0; st < C::kSteps; ++st) {
+                v4i b = {0, 0, 0, 0};
+                if (r < M)
+                    b = *reinterpret_cast<const v4i *>(act + r * kActStride +
+                                                       ul * C::kUnitCodes + 16 * st);
+                const v4i a = {c[4 * st], c[4 * st + 1], c[4 * st + 2], c[4 * st + 3]};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+            }
         }
     }
 
-    part[wave][lane] = acc;
+    __syncthreads();
+    part[wave * 64 + lane] = acc;
     __syncthreads();
     if (wave != 0) return;
-    v4i tot = part[0][lane];
+    v4i tot = part[lane];
 #pragma unroll
-    for (int w = 1; w < KS; ++w) tot += part[w][lane];
+    for (int w = 1; w < KS; ++w) tot += part[w * 64 + lane];
 
     // lane holds D[4g + i][r]: weight rows n0 + 4g + i, token r
     const int t = r;
     if (t >= M) return;
-    const float gs = gamma_p[0] * scale[t];
+    const float f = gamma_p[0] * scale[t] / 127.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t n = n0 + 4 * g + i;
         if (n >= N) continue;
         const int32_t a = tot[i];
-        const float v = ((float)a * gs) / 127.0f;
+        const float v = (float)a * f;
         if constexpr (sizeof(YT) == 4)
             y[(int64_t)t * N + n] = v;
         else
@@ -130,16 +158,32 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     }
 }
 
-template <int LAYOUT, typename YT>
+template <int LAYOUT, int KS, int NSS, typename YT>
 hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *packed,
                            const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int32_t *acc, hipStream_t s) {
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
-    constexpr int KS = 4;
+    // the partial-tile buffer aliases the activation area (needs KS*1 KiB)
+    const size_t act = (size_t)M * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
+    const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) +
+                        (act > (size_t)KS * 1024 ? act : (size_t)KS * 1024);
     dim3 grid((unsigned)((N + 15) / 16)), block(64 * KS);
-    hipLaunchKernelGGL((skinny_kernel<LAYOUT, KS, YT>), grid, block, 0, s, xq, scale, packed,
-                       gamma, (int)M, N, K, rb, y, acc);
+    auto kern = skinny_kernel<LAYOUT, KS, NSS, YT>;
+    static int lds_raised = 0;  // one flag per instantiation of this launcher
+    hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, block, smem, s, xq, scale, packed, gamma, (int)M, N, K, rb, y,
+                       acc);
     return hipGetLastError();
+}
+
+template <int LAYOUT, typename YT>
+hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *packed,
+                           const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                           int32_t *acc, hipStream_t s) {
+    // one round of 4 waves x 4 super-steps covers 4096 codes (2-bit) / 5120
+    // (base-3): 64 (80) KiB of activations at M = 16
+    return launch_skinny_t<LAYOUT, 4, 4, YT>(xq, scale, packed, gamma, M, N, K, y, acc, s);
 }
 
 }  // namespace
@@ -149,15 +193,15 @@ hipError_t launch_forward_skinny(const int8_t *xq, const float *scale, const uin
                                  void *y, int y_dtype, int32_t *acc, hipStream_t stream) {
     if (layout == kLayout2Bit) {
         if (y_dtype == kF32)
-            return launch_skinny_t<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
+            return launch_skinny_l<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
                                                 static_cast<float *>(y), acc, stream);
-        return launch_skinny_t<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
+        return launch_skinny_l<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
                                             static_cast<uint16_t *>(y), acc, stream);
     }
     if (y_dtype == kF32)
-        return launch_skinny_t<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
+        return launch_skinny_l<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
                                              static_cast<float *>(y), acc, stream);
-    return launch_skinny_t<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
+    return launch_skinny_l<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
                                          static_cast<uint16_t *>(y), acc, stream);
 }
 
