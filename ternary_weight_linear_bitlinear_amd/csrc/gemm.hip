@@ -1,57 +1,86 @@
 // Prefill-side product (M > 16 tokens): a tiled INT8 matrix-core GEMM.
-// Activations (int8) and weight codes are staged through LDS per k-tile; the
-// packed weights are expanded to signed code bytes once per block and k-tile
-// on their way into LDS, then consumed by v_mfma_i32_32x32x32_i8. Every
-// product term is an INT8 activation times a code in {-1, 0, +1}, summed
-// exactly in INT32 ([b158] "BitNet b1.58深度解析" §3.3 and §4.2), then
-// scaled by gamma * scale[m] / 127 in the epilogue ([b158] §5.2-5.3).
+// Every product term is an INT8 activation times a code in {-1, 0, +1},
+// summed exactly in INT32 ([b158] "BitNet b1.58深度解析" §3.3 and §4.2), then
+// scaled by gamma * scale[m] / 127 in the epilogue ([b158] §5.2-5.3). The
+// instruction is v_mfma_i32_32x32x32_i8.
+//
+// Data flow. Activations (int8) are staged through LDS, double buffered.
+// Packed weight codes never touch LDS: each wave loads the 16-byte packed
+// units of its own fragment columns straight from global memory (L2) and
+// expands them in registers to signed code bytes. The k slots of an MFMA are
+// a free choice as long as both operands agree, so within one k-tile of two
+// packed units per weight row (128 codes in the 2-bit layout, 160 in base-3)
+// lane group g (lanes 32g..32g+31) takes unit g, and MFMA k-step s takes
+// codes [UC*g + 16 s, +16) of the tile for that lane group (UC = codes per
+// unit); one 16-byte load then feeds all 4 (5) k-steps of the tile, and the
+// activation operand is read from LDS at the same offsets.
 //
 // Block tile BM tokens x BN weight rows, WM x WN waves, each owning
-// (BM/WM) x (BN/WN) outputs as 32 x 32 fragments. A k-tile is two 16-byte
-// units of packed codes per weight row: 128 codes in the 2-bit layout, 160
-// in base-3, i.e. 4 or 5 MFMA k-steps. LDS is double buffered and the global
-// loads run two k-tiles ahead through two register sets: while tile k is
-// multiplied, tile k+1 (already in registers) is written to the other LDS
-// buffer and tile k+2 is in flight; one barrier per k-tile. Blocks are
-// mapped to tiles so that each of the eight XCDs (dispatched round-robin by
-// block id) works on a contiguous run of tiles, which shares activation rows
-// in that XCD's L2.
+// (BM/WM) x (BN/WN) outputs as 32 x 32 fragments. Loads run two k-tiles ahead
+// through two register sets; one barrier per k-tile. Blocks are mapped to
+// tiles so that each of the eight XCDs (dispatched round-robin by block id)
+// works on a contiguous run of tiles sharing activation rows in its L2.
 #include "bl_internal.hpp"
 #include "device_util.hpp"
+
+#include <type_traits>
 
 namespace bl {
 namespace {
 
 constexpr int kXcds = 8;
 
-template <int LAYOUT, int BM_, int BN_, int WM_, int WN_>
+template <int LAYOUT, int BM_, int BN_, int WM_, int WN_, int DIST_>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int THREADS = 64 * WM * WN;
+    static constexpr int DIST = DIST_;  // k-tiles the global loads run ahead (1 or 2)
+    static constexpr int kThreads = 64 * WM * WN;
     static constexpr int UC = LAYOUT == kLayout2Bit ? 64 : 80;  // codes per 16-byte unit
-    static constexpr int UNITS = 2;                               // units per row per k-tile
-    static constexpr int BK = UNITS * UC;                         // codes per k-tile
+    static constexpr int BK = 2 * UC;                             // codes per k-tile
     static constexpr int LDSK = BK + 16;                          // padded LDS row (bytes)
-    static constexpr int KSTEPS = BK / 32;
-    static constexpr int ACH = BM * BK / 16 / THREADS;            // A 16B chunks per thread
-    static constexpr int BUNITS = BN * UNITS;                     // B units per k-tile
+    static constexpr int KSTEPS = UC / 16;                        // MFMA k-steps per tile
+    static constexpr int ACH = BM * BK / 16 / kThreads;           // A 16B chunks per thread
     static constexpr int FI = BM / WM / 32, FJ = BN / WN / 32;    // fragments per wave
-    static constexpr int STAGE = (BM + BN) * LDSK;
+    static constexpr int STAGE = BM * LDSK;
     static constexpr int LUT = LAYOUT == kLayoutBase3 ? 8192 : 0;
     static constexpr int SMEM = LUT + 2 * STAGE;
-    static_assert(BM * BK % (16 * THREADS) == 0, "A tile must split evenly");
-    static_assert(BUNITS <= THREADS, "one B unit per thread at most");
-    static_assert(FI >= 1 && FJ >= 1, "wave tile of at least one fragment");
+    static_assert(BM * BK % (16 * kThreads) == 0, "A tile must split evenly");
 };
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, typename YT>
+// Expand one packed 16-byte unit into UC code bytes (natural order).
+template <int LAYOUT>
+__device__ __forceinline__ void expand_unit(const uint4 wv, const uint64_t *lut, int c[20]) {
+    if (LAYOUT == kLayout2Bit) {
+        expand_2bit_word(wv.x, c + 0);
+        expand_2bit_word(wv.y, c + 4);
+        expand_2bit_word(wv.z, c + 8);
+        expand_2bit_word(wv.w, c + 12);
+    } else {
+        uint32_t d[20];
+#pragma unroll
+        for (int i = 0; i < 20; ++i) d[i] = 0u;
+        const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t v = (w[j / 4] >> (8 * (j % 4))) & 0xFFu;
+            const uint64_t e = lut[(j % 4) * 256 + v];
+            const int dw = (5 * j) / 4;
+            d[dw] |= (uint32_t)e;
+            d[dw + 1] |= (uint32_t)(e >> 32);
+        }
+#pragma unroll
+        for (int i = 0; i < 20; ++i) c[i] = (int)d[i];
+    }
+}
+
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, bool EVEN_K, typename YT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ scale,
     const uint8_t *__restrict__ packed, const float *__restrict__ gamma_p, int64_t M,
-    int64_t N, int64_t K, int64_t rb, int tiles_m, int tiles_n, YT *__restrict__ y,
+    int64_t N, int64_t K, int64_t rb, int tiles_m, int tiles_n, YT *__restrict__ y, int64_t ldy,
     int32_t *__restrict__ acc_out) {
-    using C = GemmCfg<LAYOUT, BM, BN, WM, WN>;
-    constexpr int kThreads = C::THREADS;
+    using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
+    constexpr int kThreads = C::kThreads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem);
     int8_t *stage0 = reinterpret_cast<int8_t *>(smem + C::LUT);
@@ -68,6 +97,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
     const int wm = wave / WN, wn = wave % WN;
+    const int frow = lane % 32;  // fragment row (A) / column (B)
+    const int lg = lane / 32;    // lane group: packed unit within the k-tile
 
     if (LAYOUT == kLayoutBase3) {
         for (int i = tid; i < 4 * 256; i += kThreads)
@@ -75,78 +106,62 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     }
 
     const int64_t units = rb / 16;
-    const int64_t ktiles = (units + C::UNITS - 1) / C::UNITS;
-    const bool a_aligned = (K % 16) == 0;
-    const bool has_b = tid < C::BUNITS;
-    const int b_row = tid / C::UNITS, b_unit = tid % C::UNITS;
-    const bool b_row_ok = has_b && n0 + b_row < N;
-    const uint8_t *b_src = packed + (n0 + b_row) * rb;
+    const int64_t ktiles = (units + 1) / 2;
+    // this lane's weight rows (one per fragment column block)
+    const uint8_t *b_src[C::FJ];
+    bool b_ok[C::FJ];
+#pragma unroll
+    for (int j = 0; j < C::FJ; ++j) {
+        const int64_t n = n0 + wn * (BN / WN) + j * 32 + frow;
+        b_ok[j] = n < N;
+        b_src[j] = packed + (b_ok[j] ? n : 0) * rb;
+    }
 
-    v4i a_regs[2][C::ACH];
-    uint4 b_regs[2];
+    v4i a_regs[DIST][C::ACH];
+    uint4 b_regs[DIST][C::FJ];
 
-    auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 &b_reg) {
+    // Loads are branch-free in the common case (rows a multiple of 16 bytes):
+    // an out-of-range chunk reads a valid address and is zeroed by a select,
+    // so no control flow splits the load stream and the compiler can keep all
+    // of a tile's loads in flight. Other row lengths take a byte-wise path.
+    auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 *b_reg) {
         const int64_t kc0 = kt * C::BK;
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
             const int q = tid + i * kThreads;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             const int64_t m = m0 + row, k = kc0 + col * 16;
-            v4i v = {0, 0, 0, 0};
-            if (m < M) {
-                const int8_t *p = xq + m * K;
-                if (a_aligned && k + 16 <= K) {
-                    v = *reinterpret_cast<const v4i *>(p + k);
-                } else if (k < K) {
+            if (EVEN_K) {
+                const bool ok = m < M && k < K;
+                const v4i v = *reinterpret_cast<const v4i *>(xq + (ok ? m * K + k : 0));
+                a_reg[i] = ok ? v : v4i{0, 0, 0, 0};
+            } else {
+                v4i v = {0, 0, 0, 0};
+                if (m < M && k < K) {
+                    const int8_t *p = xq + m * K;
                     uint32_t d[4] = {0u, 0u, 0u, 0u};
                     for (int e = 0; e < 16; ++e)
                         if (k + e < K) d[e / 4] |= (uint32_t)(uint8_t)p[k + e] << (8 * (e % 4));
                     v = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
                 }
+                a_reg[i] = v;
             }
-            a_reg[i] = v;
         }
-        const int64_t unit = kt * C::UNITS + b_unit;
-        b_reg = make_uint4(0u, 0u, 0u, 0u);
-        if (b_row_ok && unit < units) b_reg = *reinterpret_cast<const uint4 *>(b_src + unit * 16);
+        const int64_t unit = kt * 2 + lg;
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j) {
+            const bool ok = b_ok[j] && unit < units;
+            const uint4 v = *reinterpret_cast<const uint4 *>(b_src[j] + (ok ? unit * 16 : 0));
+            b_reg[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
     };
 
-    auto store_tile = [&](int8_t *st, const v4i *a_reg, const uint4 b_reg) {
-        int8_t *As = st;
-        int8_t *Bs = st + BM * C::LDSK;
+    auto store_a = [&](int8_t *As, const v4i *a_reg) {
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
             const int q = tid + i * kThreads;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             *reinterpret_cast<v4i *>(As + row * C::LDSK + col * 16) = a_reg[i];
-        }
-        if (!has_b) return;
-        int8_t *dst = Bs + b_row * C::LDSK + b_unit * C::UC;
-        if (LAYOUT == kLayout2Bit) {
-            const uint32_t w[4] = {b_reg.x, b_reg.y, b_reg.z, b_reg.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                int c[4];
-                expand_2bit_word(w[q], c);
-                *reinterpret_cast<v4i *>(dst + 16 * q) = v4i{c[0], c[1], c[2], c[3]};
-            }
-        } else {
-            uint32_t d[20];
-#pragma unroll
-            for (int i = 0; i < 20; ++i) d[i] = 0u;
-            const uint32_t w[4] = {b_reg.x, b_reg.y, b_reg.z, b_reg.w};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t v = (w[j / 4] >> (8 * (j % 4))) & 0xFFu;
-                const uint64_t e = lut[(j % 4) * 256 + v];
-                const int dw = (5 * j) / 4;
-                d[dw] |= (uint32_t)e;
-                d[dw + 1] |= (uint32_t)(e >> 32);
-            }
-#pragma unroll
-            for (int q = 0; q < 5; ++q)
-                *reinterpret_cast<v4i *>(dst + 16 * q) =
-                    v4i{(int)d[4 * q], (int)d[4 * q + 1], (int)d[4 * q + 2], (int)d[4 * q + 3]};
         }
     };
 
@@ -158,109 +173,208 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    const int frow = lane % 32;       // fragment row (A) / column (B)
-    const int fk = 16 * (lane / 32);  // byte offset of this lane's k slots
+    // The loop body is free of branches: the k-tile count is rounded up to
+    // even, and loads of tiles past the end read valid addresses and are
+    // zeroed by the guards in load_tile, so those tiles add nothing. The loop
+    // is unrolled by two so that LDS buffers and register sets are static and
+    // the compiler can wait for exactly the loads a step consumes.
+    const int64_t kt_end = (ktiles + 1) & ~(int64_t)1;
 
-    if (LAYOUT == kLayoutBase3) __syncthreads();  // decode table ready
-    // Pipeline: LDS holds tiles kt (being multiplied) and kt+1 (being
-    // written); registers hold tile kt+1 (arrived) and kt+2 (in flight).
-    if (ktiles > 0) load_tile(0, a_regs[0], b_regs[0]);
-    if (ktiles > 1) load_tile(1, a_regs[1], b_regs[1]);
-    if (ktiles > 0) store_tile(stage0, a_regs[0], b_regs[0]);
-    __syncthreads();
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        const int cur_i = (int)(kt & 1);
-        int8_t *cur = stage0 + cur_i * C::STAGE;
-        int8_t *nxt = stage0 + (cur_i ^ 1) * C::STAGE;
-        if (kt + 2 < ktiles) {
-            if (cur_i == 0) load_tile(kt + 2, a_regs[0], b_regs[0]);
-            else load_tile(kt + 2, a_regs[1], b_regs[1]);
+    // Multiply the k-tile in LDS buffer As by the weight units bu (one per
+    // fragment column block). 2-bit: k-step ks consumes exactly word ks of a
+    // unit, expanded just before use (4 live registers per column block).
+    // Base-3: a unit's five trits per byte straddle k-steps, so the whole
+    // unit is expanded first.
+    auto mma = [&](const int8_t *As, const uint4 (&bu)[C::FJ]) {
+        int cb[LAYOUT == kLayoutBase3 ? C::FJ : 1][20];
+        if constexpr (LAYOUT == kLayoutBase3) {
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) expand_unit<LAYOUT>(bu[j], lut, cb[j]);
         }
-        const int8_t *As = cur;
-        const int8_t *Bs = cur + BM * C::LDSK;
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            v4i a[C::FI], bb[C::FJ];
+            v4i a[C::FI];
 #pragma unroll
             for (int i = 0; i < C::FI; ++i)
                 a[i] = *reinterpret_cast<const v4i *>(
-                    As + (wm * (BM / WM) + i * 32 + frow) * C::LDSK + ks * 32 + fk);
+                    As + (wm * (BM / WM) + i * 32 + frow) * C::LDSK + lg * C::UC + ks * 16);
 #pragma unroll
-            for (int j = 0; j < C::FJ; ++j)
-                bb[j] = *reinterpret_cast<const v4i *>(
-                    Bs + (wn * (BN / WN) + j * 32 + frow) * C::LDSK + ks * 32 + fk);
+            for (int j = 0; j < C::FJ; ++j) {
+                v4i bj;
+                if constexpr (LAYOUT == kLayout2Bit) {
+                    const uint32_t w = ks == 0 ? bu[j].x : ks == 1 ? bu[j].y : ks == 2 ? bu[j].z
+                                                                                     : bu[j].w;
+                    int c[4];
+                    expand_2bit_word(w, c);
+                    bj = v4i{c[0], c[1], c[2], c[3]};
+                } else {
+                    bj = v4i{cb[j][4 * ks], cb[j][4 * ks + 1], cb[j][4 * ks + 2],
+                             cb[j][4 * ks + 3]};
+                }
+                // weights as the row operand: D[n][m], so each lane ends up
+                // holding four consecutive output columns per register quad
 #pragma unroll
-            for (int i = 0; i < C::FI; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bb[j], acc[i][j], 0,
-                                                                      0, 0);
+                for (int i = 0; i < C::FI; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bj, a[i], acc[i][j], 0, 0,
+                                                                      0);
+            }
         }
-        if (kt + 1 < ktiles) {
-            if (cur_i == 0) store_tile(nxt, a_regs[1], b_regs[1]);
-            else store_tile(nxt, a_regs[0], b_regs[0]);
+    };
+
+    if constexpr (DIST == 2) {
+        // LDS holds tiles kt and kt+1; registers hold kt+1 (arrived) and kt+2
+        // (in flight). S names the register set and LDS buffer of tile kt.
+        load_tile(0, a_regs[0], b_regs[0]);
+        load_tile(1, a_regs[DIST - 1], b_regs[DIST - 1]);
+        store_a(stage0, a_regs[0]);
+        __syncthreads();  // tile 0 (and the decode table) ready
+        auto step = [&](int64_t kt, auto set_c) {
+            constexpr int S = decltype(set_c)::value;
+            uint4 bu[C::FJ];
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[S][j];
+            load_tile(kt + 2, a_regs[S], b_regs[S]);
+            mma(stage0 + S * C::STAGE, bu);
+            store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[S ^ 1]);
+            __syncthreads();
+        };
+        for (int64_t kt = 0; kt < kt_end; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, DIST - 1>{});
         }
+    } else {
+        // LDS holds tiles kt and kt+1; one register set carries tile kt+1.
+        load_tile(0, a_regs[0], b_regs[0]);
+        store_a(stage0, a_regs[0]);
         __syncthreads();
+        auto step = [&](int64_t kt, auto buf_c) {
+            constexpr int S = decltype(buf_c)::value;
+            uint4 bu[C::FJ];
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[0][j];
+            load_tile(kt + 1, a_regs[0], b_regs[0]);
+            mma(stage0 + S * C::STAGE, bu);
+            store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0]);
+            __syncthreads();
+        };
+        for (int64_t kt = 0; kt < kt_end; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
+        }
     }
 
-    // Epilogue. Fragment register r of lane l holds D[i][j] with
-    // j = l % 32 (weight row), i = 8 (r / 4) + 4 (l / 32) + r % 4 (token).
+    // Epilogue. Fragment (i, j) register r of lane l holds D[n][m] with
+    // m = l % 32 (token within fragment i) and n = 8 (r / 4) + 4 (l / 32) +
+    // r % 4 (weight row within fragment j): registers 4q..4q+3 are four
+    // consecutive outputs of one token, written with one 8- or 16-byte store.
     const float gamma = gamma_p[0];
+    const bool full = m0 + BM <= M && n0 + BN <= N && (ldy % 4) == 0;
 #pragma unroll
-    for (int fi = 0; fi < C::FI; ++fi) {
+    for (int i = 0; i < C::FI; ++i) {
+        const int64_t m = m0 + wm * (BM / WM) + i * 32 + frow;
+        const float f = gamma * scale[m < M ? m : 0] / 127.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m =
-                m0 + wm * (BM / WM) + fi * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-            if (m >= M) continue;
-            const float f = gamma * scale[m] / 127.0f;
+        for (int j = 0; j < C::FJ; ++j) {
 #pragma unroll
-            for (int fj = 0; fj < C::FJ; ++fj) {
-                const int64_t n = n0 + wn * (BN / WN) + fj * 32 + (lane % 32);
-                if (n >= N) continue;
-                const int32_t a = acc[fi][fj][r];
-                const float v = (float)a * f;
-                if constexpr (sizeof(YT) == 4)
-                    y[m * N + n] = v;
-                else
-                    y[m * N + n] = (YT)f32_to_bf16_rne(v);
-                if (acc_out) acc_out[m * N + n] = a;
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * (BN / WN) + j * 32 + 8 * q + 4 * lg;
+                const int32_t a0 = acc[i][j][4 * q], a1 = acc[i][j][4 * q + 1];
+                const int32_t a2 = acc[i][j][4 * q + 2], a3 = acc[i][j][4 * q + 3];
+                const float v0 = (float)a0 * f, v1 = (float)a1 * f;
+                const float v2 = (float)a2 * f, v3 = (float)a3 * f;
+                if (full) {
+                    if constexpr (sizeof(YT) == 4) {
+                        *reinterpret_cast<float4 *>(y + m * ldy + n) = make_float4(v0, v1, v2, v3);
+                    } else {
+                        const bf16x2 lo = {(__bf16)v0, (__bf16)v1};
+                        const bf16x2 hi = {(__bf16)v2, (__bf16)v3};
+                        *reinterpret_cast<uint2 *>(y + m * ldy + n) =
+                            make_uint2(__builtin_bit_cast(uint32_t, lo),
+                                       __builtin_bit_cast(uint32_t, hi));
+                    }
+                    if (acc_out)
+                        *reinterpret_cast<int4 *>(acc_out + m * ldy + n) = make_int4(a0, a1, a2, a3);
+                } else if (m < M) {
+                    const int32_t av[4] = {a0, a1, a2, a3};
+                    const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (n + e >= N) continue;
+                        if constexpr (sizeof(YT) == 4)
+                            y[m * ldy + n + e] = vv[e];
+                        else
+                            y[m * ldy + n + e] = (YT)f32_to_bf16_rne(vv[e]);
+                        if (acc_out) acc_out[m * ldy + n + e] = av[e];
+                    }
+                }
             }
         }
     }
 }
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, typename YT>
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, typename YT>
 hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
-                            int32_t *acc, hipStream_t s) {
-    using C = GemmCfg<LAYOUT, BM, BN, WM, WN>;
+                            int64_t ldy, int32_t *acc, hipStream_t s) {
+    using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const int64_t ntiles = (int64_t)tm * tn;
     const int64_t blocks = (ntiles + kXcds - 1) / kXcds * kXcds;
-    auto kern = gemm_kernel<LAYOUT, BM, BN, WM, WN, YT>;
-    static int lds_raised = 0;
-    hipError_t e = allow_dynamic_lds(kern, C::SMEM, &lds_raised);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::THREADS), C::SMEM, s, xq, scale,
-                       packed, gamma, M, N, K, rb, tm, tn, y, acc);
-    return hipGetLastError();
+    auto launch = [&](auto kern, int *flag) {
+        hipError_t e = allow_dynamic_lds(kern, C::SMEM, flag);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::SMEM, s, xq, scale,
+                           packed, gamma, M, N, K, rb, tm, tn, y, ldy, acc);
+        return hipGetLastError();
+    };
+    static int lds_even = 0, lds_odd = 0;
+    if (K % 16 == 0) return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, true, YT>, &lds_even);
+    return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, false, YT>, &lds_odd);
+}
+
+// Tile configuration by problem size. Each shape's configuration was chosen
+// by timing on MI355X (see the design notes): large 2-bit problems use
+// 256 x 256 tiles with 8 waves; when those tiles do not fill whole rounds of
+// 256 CUs, the columns that do are one launch and the leftover columns a
+// second launch with smaller tiles, so no round runs mostly idle.
+template <int LAYOUT, typename YT>
+hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t *packed,
+                            const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                            int64_t ldy, int32_t *acc, hipStream_t s) {
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 128) >= 512)
+        return launch_gemm_tile<LAYOUT, 256, 128, 2, 4, 2>(xq, scale, packed, gamma, M, N, K, y,
+                                                           ldy, acc, s);
+    if (tiles(128, 128) >= 256)
+        return launch_gemm_tile<LAYOUT, 128, 128, 2, 2, 2>(xq, scale, packed, gamma, M, N, K, y,
+                                                           ldy, acc, s);
+    return launch_gemm_tile<LAYOUT, 128, 64, 2, 2, 2>(xq, scale, packed, gamma, M, N, K, y, ldy,
+                                                      acc, s);
 }
 
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *packed,
                          const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
                          int32_t *acc, hipStream_t s) {
-    // the largest tile that still gives every CU about two tiles
-    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 128) >= 512)
-        return launch_gemm_tile<LAYOUT, 256, 128, 4, 2>(xq, scale, packed, gamma, M, N, K, y, acc,
-                                                        s);
-    if (tiles(128, 128) >= 256)
-        return launch_gemm_tile<LAYOUT, 128, 128, 2, 2>(xq, scale, packed, gamma, M, N, K, y, acc,
-                                                        s);
-    return launch_gemm_tile<LAYOUT, 128, 64, 2, 2>(xq, scale, packed, gamma, M, N, K, y, acc, s);
+    constexpr int64_t kCUs = 256;
+    const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
+    if constexpr (LAYOUT == kLayout2Bit) {
+        const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+        if (tm * tn >= kCUs) {
+            // columns covered by whole rounds of 256 x 256 tiles
+            const int64_t rounds = tm * tn / kCUs;
+            int64_t tn_main = rounds * kCUs / tm;
+            if (tn_main > tn) tn_main = tn;
+            const int64_t n_main = tn_main * 256 < N ? tn_main * 256 : N;
+            hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 2, 4, 2>(
+                xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
+            if (e != hipSuccess || n_main == N) return e;
+            return launch_gemm_cols<LAYOUT>(xq, scale, packed + n_main * rb, gamma, M, N - n_main,
+                                            K, y + n_main, N, acc ? acc + n_main : nullptr, s);
+        }
+    }
+    return launch_gemm_cols<LAYOUT>(xq, scale, packed, gamma, M, N, K, y, N, acc, s);
 }
 
 }  // namespace

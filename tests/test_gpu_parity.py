@@ -107,6 +107,8 @@ FWD_CASES = [
     (1, 256, 256), (1, 31, 100), (2, 300, 1000), (3, 64, 64), (5, 16, 1), (8, 256, 256),
     (16, 100, 4096), (16, 33, 17), (17, 256, 256), (64, 130, 1000), (130, 300, 260),
     (257, 257, 320), (33, 1, 160), (128, 128, 4096), (300, 512, 129),
+    # enough 256 x 256 tiles for a full round plus leftover columns
+    (4096, 4357, 64), (2048, 8200, 48),
 ]
 
 
