@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", default="", help="comma list of rows to run (profiling runs)")
+    ap.add_argument("--mode", default="full", choices=["full", "profile"],
+                    help="profile: only the fused decode kernel (64 launches over rotating "
+                         "weight copies) and a 512 MiB device copy, for counter runs")
     return ap.parse_args()
 
 
@@ -108,6 +111,23 @@ def main():
 
     rows = {}
 
+    if args.mode == "profile":
+        p = synth.workload("decode")
+        W = to_dev(p.w_store, True)
+        x = to_dev(p.x_store, True)
+        packed, gamma = bl.bitlinear_pack_weights(W, "2bit")
+        copies = [packed.clone() for _ in range(args.copies)]
+        y = torch.empty((1, p.N), dtype=torch.float32, device=dev)
+        for i in range(64):
+            bl.bitlinear_linear(x, copies[i % args.copies], gamma, p.N, "2bit", y=y)
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)  # calibration: reads and writes exactly 512 MiB
+        torch.cuda.synchronize()
+        log("profile mode done")
+        return
+
     # ---------------------------------------------------------------- decode
     log("decode workload: generating inputs")
     p = synth.workload("decode")
@@ -130,7 +150,12 @@ def main():
         rb = packed.shape[1]
         wbytes = p.N * rb
 
-        def step(i, copies=copies, gamma=gamma, layout=layout, y=y, xq=xq, sc=sc):
+        def step(i, copies=copies, gamma=gamma, layout=layout, y=y):
+            # one token through one layer: fused quantise + multiply (one launch)
+            r = i % R
+            bl.bitlinear_linear(xs[r], copies[r], gamma, p.N, layout, y=y)
+
+        def step_two(i, copies=copies, gamma=gamma, layout=layout, y=y, xq=xq, sc=sc):
             r = i % R
             bl.bitlinear_quant_acts(xs[r], xq=xq, scale=sc)
             bl.bitlinear_forward(xq, sc, copies[r], gamma, p.N, p.K, layout, y=y)
@@ -143,18 +168,41 @@ def main():
             step(i)
         # the timed region is one graph replay of exactly `steps` steps
         ms_step = graph_ms(step, args.steps)
+        ms_two = graph_ms(step_two, args.steps)
         k_mean = graph_ms(gemv, 2 * R)
-        alg = wbytes + p.K + 4 + 4 + 4 * p.N
+        # fused kernel: packed weights + bf16 x + gamma + fp32 y
+        alg = wbytes + 2 * p.K + 4 + 4 * p.N
         decode[layout] = dict(ms_per_step=ms_step, weight_bytes=wbytes,
                               weight_gbs=wbytes / (ms_step * 1e-3) / 1e9,
-                              gemv_ms_mean=k_mean,
-                              gemv_alg_bytes=alg,
-                              gemv_gbs=alg / (k_mean * 1e-3) / 1e9)
-        log(f"decode {layout}: step {ms_step*1e3:.2f} us, gemv {k_mean*1e3:.2f} us "
-            f"({decode[layout]['gemv_gbs']:.0f} GB/s)")
+                              fused_alg_bytes=alg,
+                              fused_gbs=alg / (ms_step * 1e-3) / 1e9,
+                              two_launch_ms_per_step=ms_two,
+                              forward_only_ms=k_mean,
+                              forward_only_gbs=(wbytes + p.K + 8 + 4 * p.N) / (k_mean * 1e-3) / 1e9)
+        log(f"decode {layout}: fused step {ms_step*1e3:.2f} us ({decode[layout]['fused_gbs']:.0f} GB/s), "
+            f"two-launch step {ms_two*1e3:.2f} us, forward only {k_mean*1e3:.2f} us")
         del copies
         torch.cuda.empty_cache()
     rows["decode_gemv"] = decode
+
+    # Weight streaming at a size where launch latency no longer dominates:
+    # one token against a 32768 x 4096 ternary matrix (32 MiB packed, the
+    # shape of a vocabulary projection), 16 rotating copies.
+    if want("stream"):
+        ps = synth.make_problem(M=1, N=32768, K=4096, seed=9, dtype="bf16", outlier_frac=0.01)
+        pk, g = bl.bitlinear_pack_weights(to_dev(ps.w_store, True), "2bit")
+        cps = [pk.clone() for _ in range(16)]
+        xs1 = to_dev(ps.x_store, True)
+        ys = torch.empty((1, ps.N), dtype=torch.float32, device=dev)
+        f = lambda i: bl.bitlinear_linear(xs1, cps[i % 16], g, ps.N, "2bit", y=ys)
+        ms = graph_ms(f, 64)
+        alg = pk.numel() + 2 * ps.K + 4 + 4 * ps.N
+        rows["decode_stream_32768x4096"] = dict(ms=ms, alg_bytes=alg,
+                                               gbs=alg / (ms * 1e-3) / 1e9,
+                                               frac_hbm=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        log(f"stream 32768x4096: {ms*1e3:.2f} us = {alg/(ms*1e-3)/1e9:.0f} GB/s")
+        del cps
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ pack
     if want("pack"):
@@ -256,18 +304,20 @@ def main():
 
     # ------------------------------------------------------------ roofline
     d2 = decode["2bit"]
-    roof = {"kernel": "skinny_kernel<2bit> (decode GEMV, M=1, 4096x4096)", "bound": "hbm",
-            "achieved": d2["gemv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": d2["gemv_gbs"] / HBM_PEAK_GBS, "traffic": None,
-            "alg_bytes_per_launch": d2["gemv_alg_bytes"],
-            "launch_ms_mean": d2["gemv_ms_mean"]}
-    counters = os.path.join(ROOT, "profiles", "gemv_2bit_decode_counters.json")
+    roof = {"kernel": "linear_decode_kernel<2bit> (fused decode step, M=1, 4096x4096)",
+            "bound": "hbm", "achieved": d2["fused_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": d2["fused_gbs"] / HBM_PEAK_GBS, "traffic": None,
+            "alg_bytes_per_launch": d2["fused_alg_bytes"],
+            "launch_ms_mean": d2["ms_per_step"]}
+    counters = os.path.join(ROOT, "profiles", "decode_fused_2bit_counters.json")
     if os.path.exists(counters):
         with open(counters) as f:
             c = json.load(f)
         src = os.path.join(ROOT, "ternary_weight_linear_bitlinear_amd", "csrc", "skinny.hip")
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if c.get("source_sha") == sha:
+        if not os.path.exists(src):
+            src = None
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] if src else None
+        if sha and c.get("source_sha") == sha:
             roof["traffic"] = c.get("hbm_bytes_per_launch")
 
     ms = d2["ms_per_step"]
@@ -278,7 +328,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode GEMV: M=1 token, W 4096x4096 bf16 ~N(0,0.02) quantised "
                                "once (absmean ternary, 2-bit packed), x bf16 ~N(0,1) + 1% +/-20 "
-                               "outliers; step = quant_acts + forward; 128 rotating weight copies",
+                               "outliers; step = per-token INT8 quantisation + integer product + "
+                               "dequant (one fused launch); 128 rotating weight copies",
                    "M": 1, "K": 4096, "N": 4096, "layout": "2bit", "out": "fp32"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -131,6 +131,20 @@ bl_status bitlinear_forward(const int8_t *xq, const float *scale,
                             int64_t M, int64_t N, int64_t K,
                             void *y, int y_dtype, int32_t *acc, void *stream);
 
+/* Fused decode step: per-token INT8 quantisation of x (exactly as
+ * bitlinear_quant_acts) and the product with its epilogue (exactly as
+ * bitlinear_forward) in one launch, for the latency-bound decode regime.
+ *   x       [M, K] x_dtype (BL_F32 or BL_BF16), read only.
+ *   packed  [N, row_bytes] in `layout`; gamma: 1 float (device).
+ *   y       out: [M, N] y_dtype; acc: optional out [M, N] int32, or NULL.
+ * Only 1 <= M <= 4 is supported: every workgroup re-derives the token scales
+ * from x, which pays off only for a handful of tokens. Larger M returns
+ * BL_ERR_UNSUPPORTED (use bitlinear_quant_acts + bitlinear_forward).
+ * Sources as for bitlinear_quant_acts and bitlinear_forward. */
+bl_status bitlinear_linear(const void *x, int x_dtype, const uint8_t *packed, int layout,
+                           const float *gamma, int64_t M, int64_t N, int64_t K,
+                           void *y, int y_dtype, int32_t *acc, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *bitlinear_status_string(int status);
 

@@ -45,6 +45,8 @@ _lib.bitlinear_quant_acts.restype = _int
 _lib.bitlinear_quant_acts.argtypes = [_p, _int, _i64, _i64, _p, _p, _p]
 _lib.bitlinear_forward.restype = _int
 _lib.bitlinear_forward.argtypes = [_p, _p, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
+_lib.bitlinear_linear.restype = _int
+_lib.bitlinear_linear.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
 _lib.bitlinear_status_string.restype = ctypes.c_char_p
 _lib.bitlinear_status_string.argtypes = [_int]
 _lib.bitlinear_version.restype = _int
@@ -52,7 +54,8 @@ _lib.bitlinear_version.argtypes = []
 
 EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
             "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
-            "bitlinear_status_string", "bitlinear_version"]
+            "bitlinear_linear", "bitlinear_status_string", "bitlinear_version"]
+FUSED_MAX_M = 4
 
 
 class BitLinearError(RuntimeError):
@@ -160,9 +163,30 @@ def bitlinear_forward(xq: torch.Tensor, scale: torch.Tensor, packed: torch.Tenso
     return (y, acc) if want_acc else y
 
 
+def bitlinear_linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
+                     layout="2bit", out_dtype=torch.float32, y: torch.Tensor | None = None,
+                     acc: torch.Tensor | bool | None = None, stream=None):
+    """Fused quantise + multiply for M <= 4 tokens; returns y, or (y, acc)."""
+    assert x.dim() == 2 and x.is_contiguous() and x.dtype in _DTYPES
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    want_acc = acc is not None and acc is not False
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    _check(_lib.bitlinear_linear(_ptr(x), _DTYPES[x.dtype], _ptr(packed), _layout(layout),
+                                 _ptr(gamma), M, N, K, _ptr(y), _DTYPES[y.dtype],
+                                 _ptr(acc) if want_acc else None, _stream(stream)),
+           "bitlinear_linear")
+    return (y, acc) if want_acc else y
+
+
 def linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int, layout="2bit",
            out_dtype=torch.float32, stream=None) -> torch.Tensor:
-    """BitLinear forward of x [M, K] against packed weights: quantise, then multiply."""
+    """BitLinear forward of x [M, K] against packed weights: one fused launch for
+    M <= 4, otherwise quantise then multiply."""
+    if x.shape[0] <= FUSED_MAX_M:
+        return bitlinear_linear(x, packed, gamma, N, layout, out_dtype, stream=stream)
     xq, scale = bitlinear_quant_acts(x, stream=stream)
     return bitlinear_forward(xq, scale, packed, gamma, N, x.shape[1], layout, out_dtype,
                              stream=stream)

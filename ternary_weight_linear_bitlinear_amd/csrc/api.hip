@@ -121,6 +121,24 @@ bl_status bitlinear_forward(const int8_t *xq, const float *scale, const uint8_t 
         bl::launch_forward_gemm(xq, scale, packed, layout, gamma, M, N, K, y, y_dtype, acc, s));
 }
 
+bl_status bitlinear_linear(const void *x, int x_dtype, const uint8_t *packed, int layout,
+                           const float *gamma, int64_t M, int64_t N, int64_t K, void *y,
+                           int y_dtype, int32_t *acc, void *stream) {
+    if (!x || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(gamma) || !aligned16(y) ||
+        (acc && !aligned16(acc)))
+        return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || K > kMaxK || N > 2147483647LL) return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype) || !valid_layout(layout) || !valid_dtype(y_dtype))
+        return BL_ERR_INVALID_ARG;
+    if (M > bl::fused_decode_max_m()) return BL_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    return launched(bl::launch_linear_decode(x, x_dtype, packed, layout, gamma, M, N, K, y,
+                                             y_dtype, acc, static_cast<hipStream_t>(stream)));
+}
+
 const char *bitlinear_status_string(int status) {
     switch (status) {
         case BL_OK: return "ok";

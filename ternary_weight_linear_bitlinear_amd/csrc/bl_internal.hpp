@@ -53,6 +53,11 @@ hipError_t launch_forward_skinny(const int8_t *xq, const float *scale,
                                  const float *gamma, int64_t M, int64_t N,
                                  int64_t K, void *y, int y_dtype, int32_t *acc,
                                  hipStream_t stream);
+// Fused per-token quantisation + product for M <= fused_decode_max_m().
+int64_t fused_decode_max_m();
+hipError_t launch_linear_decode(const void *x, int x_dtype, const uint8_t *packed, int layout,
+                                const float *gamma, int64_t M, int64_t N, int64_t K, void *y,
+                                int y_dtype, int32_t *acc, hipStream_t stream);
 hipError_t launch_forward_gemm(const int8_t *xq, const float *scale,
                                const uint8_t *packed, int layout,
                                const float *gamma, int64_t M, int64_t N,

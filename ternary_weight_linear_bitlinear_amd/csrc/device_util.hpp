@@ -49,6 +49,17 @@ __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
     }
 }
 
+// One activation code: q = clamp(rint((x / s) * 127), -127, 127) with IEEE
+// fp32 division (HIP's default), then the multiply, then round half to even,
+// in the order the pages write it ([b158] §3.2 and §5.2).
+__device__ __forceinline__ int8_t quant1(float x, float s) {
+    float t = x / s;
+    t = t * 127.0f;
+    float q = rintf(t);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int8_t)(int)q;
+}
+
 // Wave-wide (64 lanes) reductions through cross-lane shuffles.
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

@@ -218,17 +218,8 @@ __global__ __launch_bounds__(kThreads) void pack_base3_kernel(
 // Per-token INT8 quantisation. One block per token row; thread t owns the
 // 8-element chunks t, t + 256, ..., kept in registers between the max
 // reduction and the quantisation (J chunks per thread; J = 0 re-reads the
-// row from cache for rows longer than 8 * 256 * 8 elements).
-// q = clamp(rint((x / s) * 127), -127, 127): IEEE fp32 division, then the
-// multiply, then round half to even, exactly in the order the pages write it.
-__device__ __forceinline__ int8_t quant1(float x, float s) {
-    float t = x / s;  // correctly rounded (HIP's default fp32 division)
-    t = t * 127.0f;
-    float q = rintf(t);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int8_t)(int)q;
-}
-
+// row from cache for rows longer than 8 * 256 * 8 elements). Each code is
+// quant1() (device_util.hpp): division, then * 127, then round half to even.
 __device__ __forceinline__ float block_max(float v) {
     __shared__ float red[kThreads / 64];
     v = wave_max(v);

@@ -119,3 +119,16 @@ def test_no_device_reports_device_error(bl):
     assert _pack(bl) == bl.BL_ERR_DEVICE
     assert _quant(bl) == bl.BL_ERR_DEVICE
     assert _fwd(bl) == bl.BL_ERR_DEVICE
+
+
+def test_fused_linear_rejects_and_limits(bl):
+    lib = bl.library()
+    f = lambda **kw: lib.bitlinear_linear(kw.get("x", P), 0, P, kw.get("layout", 0), P,
+                                          kw.get("M", 1), 8, kw.get("K", 64), kw.get("y", P), 0,
+                                          None, None)
+    assert f(x=None) == bl.BL_ERR_INVALID_ARG
+    assert f(y=P + 4) == bl.BL_ERR_INVALID_ARG
+    assert f(K=0) == bl.BL_ERR_INVALID_ARG
+    assert f(layout=9) == bl.BL_ERR_INVALID_ARG
+    assert f(M=5) == bl.BL_ERR_UNSUPPORTED  # fused path covers M <= 4 only
+    assert f(M=0) == bl.BL_OK

@@ -236,3 +236,35 @@ def test_zero_activation_row_gives_zero_output(bl):
     assert got["scale"][4] == np.float32(1e-6)
     assert not got["xq"][4].any() and not got["acc"][4].any()
     assert torch.all(got["y"][4] == 0)
+
+
+# ----------------------------------------------------------------------------
+# Fused decode step (quantise + multiply in one launch)
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
+@pytest.mark.parametrize("M,N,K,dtype", [(1, 256, 256, "f32"), (2, 100, 1000, "bf16"),
+                                         (3, 33, 17, "f32"), (4, 300, 4099, "bf16"),
+                                         (1, 4096, 11008, "bf16"), (4, 64, 8192, "f32")])
+def test_fused_linear_parity(bl, layout, M, N, K, dtype):
+    """Same activation codes as the stand-alone quantiser (bit-exact), hence
+    the same INT32 accumulators as the oracle, and y within tolerance."""
+    banner(f"fused {layout} M={M} N={N} K={K} {dtype}")
+    p = synth.make_problem(M=M, N=N, K=K, seed=300 + M + N + K, dtype=dtype, outlier_frac=0.01)
+    bf = dtype == "bf16"
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, bf), layout)
+    y, acc = bl.bitlinear_linear(dev(p.x_store, bf), packed, gamma, N, layout, acc=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(p.w, p.x, layout)
+    got = dict(packed=to_np(packed), gamma=to_np(gamma)[0], xq=ref["xq"], scale=ref["scale"],
+               acc=to_np(acc), y=y)
+    assert check_end_to_end(got, ref, p, layout, torch.float32) == 0
+
+
+def test_fused_linear_decode_full(bl):
+    """The decode workload (M=1, 4096 x 4096, bf16, outliers) through the fused path."""
+    p = synth.workload("decode")
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, True), "2bit")
+    y, acc = bl.bitlinear_linear(dev(p.x_store, True), packed, gamma, p.N, "2bit", acc=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(p.w, p.x, "2bit")
+    assert np.array_equal(to_np(acc), ref["acc"])
+    check_y_f32(to_np(y), ref["y64"])
