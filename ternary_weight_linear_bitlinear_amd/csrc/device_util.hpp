@@ -60,6 +60,17 @@ __device__ __forceinline__ int8_t quant1(float x, float s) {
     return (int8_t)(int)q;
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations (so its LDS writes are visible and its LDS reads have returned),
+// then s_barrier. Unlike __syncthreads() it does not wait for outstanding
+// global loads into registers, so prefetches issued before it stay in flight.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+// Only for barriers whose purpose is LDS reuse; global memory written before
+// it is not made visible to other waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Wave-wide (64 lanes) reductions through cross-lane shuffles.
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

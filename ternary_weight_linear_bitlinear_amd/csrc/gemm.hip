@@ -124,14 +124,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     // an out-of-range chunk reads a valid address and is zeroed by a select,
     // so no control flow splits the load stream and the compiler can keep all
     // of a tile's loads in flight. Other row lengths take a byte-wise path.
-    auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 *b_reg) {
+    // Interior tiles (whole tile inside M and N, and an even number of full
+    // k-tiles) load without guards: the k-tile index is clamped so that the
+    // prefetches past the last tile re-read a valid tile whose data is never
+    // used. Edge tiles zero out-of-range chunks: they read a valid address and
+    // select zero, so no branch splits the load stream. Rows that are not a
+    // multiple of 16 bytes take a byte-wise path.
+    auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 *b_reg, auto guard_c) {
+        constexpr bool G = decltype(guard_c)::value;
+        if (!G) kt = kt < ktiles ? kt : ktiles - 1;
         const int64_t kc0 = kt * C::BK;
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
             const int q = tid + i * kThreads;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             const int64_t m = m0 + row, k = kc0 + col * 16;
-            if (EVEN_K) {
+            if (!G) {
+                a_reg[i] = *reinterpret_cast<const v4i *>(xq + m * K + k);
+            } else if (EVEN_K) {
                 const bool ok = m < M && k < K;
                 const v4i v = *reinterpret_cast<const v4i *>(xq + (ok ? m * K + k : 0));
                 a_reg[i] = ok ? v : v4i{0, 0, 0, 0};
@@ -150,9 +160,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         const int64_t unit = kt * 2 + lg;
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
-            const bool ok = b_ok[j] && unit < units;
-            const uint4 v = *reinterpret_cast<const uint4 *>(b_src[j] + (ok ? unit * 16 : 0));
-            b_reg[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+            if (!G) {
+                b_reg[j] = *reinterpret_cast<const uint4 *>(b_src[j] + unit * 16);
+            } else {
+                const bool ok = b_ok[j] && unit < units;
+                const uint4 v =
+                    *reinterpret_cast<const uint4 *>(b_src[j] + (ok ? unit * 16 : 0));
+                b_reg[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
     };
 
@@ -221,47 +236,55 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         }
     };
 
-    if constexpr (DIST == 2) {
-        // LDS holds tiles kt and kt+1; registers hold kt+1 (arrived) and kt+2
-        // (in flight). S names the register set and LDS buffer of tile kt.
-        load_tile(0, a_regs[0], b_regs[0]);
-        load_tile(1, a_regs[DIST - 1], b_regs[DIST - 1]);
-        store_a(stage0, a_regs[0]);
-        __syncthreads();  // tile 0 (and the decode table) ready
-        auto step = [&](int64_t kt, auto set_c) {
-            constexpr int S = decltype(set_c)::value;
-            uint4 bu[C::FJ];
-#pragma unroll
-            for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[S][j];
-            load_tile(kt + 2, a_regs[S], b_regs[S]);
-            mma(stage0 + S * C::STAGE, bu);
-            store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[S ^ 1]);
+    auto run = [&](auto guard_c) {
+        if constexpr (DIST == 2) {
+            // LDS holds tiles kt and kt+1; registers hold kt+1 (arrived) and kt+2
+            // (in flight). S names the register set and LDS buffer of tile kt.
+            load_tile(0, a_regs[0], b_regs[0], guard_c);
+            load_tile(1, a_regs[DIST - 1], b_regs[DIST - 1], guard_c);
+            store_a(stage0, a_regs[0]);
+            __syncthreads();  // tile 0 (and the decode table) ready
+            auto step = [&](int64_t kt, auto set_c) {
+                constexpr int S = decltype(set_c)::value;
+                uint4 bu[C::FJ];
+    #pragma unroll
+                for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[S][j];
+                load_tile(kt + 2, a_regs[S], b_regs[S], guard_c);
+                mma(stage0 + S * C::STAGE, bu);
+                store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[S ^ 1]);
+                lds_barrier();
+            };
+            for (int64_t kt = 0; kt < kt_end; kt += 2) {
+                step(kt, std::integral_constant<int, 0>{});
+                step(kt + 1, std::integral_constant<int, DIST - 1>{});
+            }
+        } else {
+            // LDS holds tiles kt and kt+1; one register set carries tile kt+1.
+            load_tile(0, a_regs[0], b_regs[0], guard_c);
+            store_a(stage0, a_regs[0]);
             __syncthreads();
-        };
-        for (int64_t kt = 0; kt < kt_end; kt += 2) {
-            step(kt, std::integral_constant<int, 0>{});
-            step(kt + 1, std::integral_constant<int, DIST - 1>{});
+            auto step = [&](int64_t kt, auto buf_c) {
+                constexpr int S = decltype(buf_c)::value;
+                uint4 bu[C::FJ];
+    #pragma unroll
+                for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[0][j];
+                load_tile(kt + 1, a_regs[0], b_regs[0], guard_c);
+                mma(stage0 + S * C::STAGE, bu);
+                store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0]);
+                lds_barrier();
+            };
+            for (int64_t kt = 0; kt < kt_end; kt += 2) {
+                step(kt, std::integral_constant<int, 0>{});
+                step(kt + 1, std::integral_constant<int, 1>{});
+            }
         }
-    } else {
-        // LDS holds tiles kt and kt+1; one register set carries tile kt+1.
-        load_tile(0, a_regs[0], b_regs[0]);
-        store_a(stage0, a_regs[0]);
-        __syncthreads();
-        auto step = [&](int64_t kt, auto buf_c) {
-            constexpr int S = decltype(buf_c)::value;
-            uint4 bu[C::FJ];
-#pragma unroll
-            for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[0][j];
-            load_tile(kt + 1, a_regs[0], b_regs[0]);
-            mma(stage0 + S * C::STAGE, bu);
-            store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0]);
-            __syncthreads();
-        };
-        for (int64_t kt = 0; kt < kt_end; kt += 2) {
-            step(kt, std::integral_constant<int, 0>{});
-            step(kt + 1, std::integral_constant<int, 1>{});
-        }
-    }
+
+    };
+    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 4) == 0;
+    if (interior)
+        run(std::integral_constant<bool, false>{});
+    else
+        run(std::integral_constant<bool, true>{});
 
     // Epilogue. Fragment (i, j) register r of lane l holds D[n][m] with
     // m = l % 32 (token within fragment i) and n = 8 (r / 4) + 4 (l / 32) +
