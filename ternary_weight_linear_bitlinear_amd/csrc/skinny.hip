@@ -6,8 +6,8 @@
 // nothing ([b158] "BitNet b1.58深度解析" §4.2); the sums are exact INT32
 // ([b158] §3.3), then scaled by gamma * scale[m] / 127 ([b158] §5.2-5.3).
 //
-// Work split: a block owns 16 consecutive weight rows; its KS waves split the
-// row length K. One "super-step" of a wave covers four 16-byte units of
+// Work split: a block owns 16 consecutive weight rows (16 * RG for batches);
+// its KS waves split the row length K. One "super-step" of a wave covers four 16-byte units of
 // packed codes per row (64 codes per unit in the 2-bit layout, 80 in base-3),
 // one unit per 16-lane group; the matrix-core k slots of lane group g are
 // mapped to that unit's codes and the activation operand is read with the
@@ -21,6 +21,34 @@
 
 namespace bl {
 namespace {
+
+// Launch shapes (measured on MI355X with the weights streamed from HBM):
+// eight waves per workgroup, each keeping two 16-byte weight loads per lane
+// in flight, beat four waves with four loads (shorter serial expand/multiply
+// chain per wave once the data lands). Batches at N >= 8192 put two row
+// groups in a workgroup, halving the activation staging per weight byte.
+constexpr int kSkKS = 8, kSkNSS = 2, kSkRG2MinN = 8192;
+constexpr int kFdKS = 8, kFdNSS = 2;
+
+// 16 elements of x held as raw 16-byte pieces (two for bf16, four for fp32),
+// widened to fp32.
+__device__ __forceinline__ void unpack_raw(const uint4 (&p)[2], float v[16]) {
+    const uint32_t w[8] = {p[0].x, p[0].y, p[0].z, p[0].w, p[1].x, p[1].y, p[1].z, p[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void unpack_raw(const uint4 (&p)[4], float v[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[4 * i] = __uint_as_float(p[i].x);
+        v[4 * i + 1] = __uint_as_float(p[i].y);
+        v[4 * i + 2] = __uint_as_float(p[i].z);
+        v[4 * i + 3] = __uint_as_float(p[i].w);
+    }
+}
 
 template <int LAYOUT>
 struct SkinnyCfg {
@@ -54,15 +82,28 @@ __device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut,
     }
 }
 
-template <int LAYOUT, int KS, int NSS, typename YT>
+// RG row groups of 16 weight rows per workgroup share every activation read
+// from LDS (one operand load feeds RG matrix-core instructions); RG > 1 pays
+// off for batches, where activations outweigh the packed weights per row.
+// MAXM bounds the batch, so the registers that carry a round's activation
+// slice into LDS are sized at compile time.
+//
+// Order within a round: the activation slice (L2-resident, small) is loaded
+// into registers first, then the weight loads are issued. Vector-memory
+// counters complete in issue order, so the wait for the activations leaves
+// every weight load in flight, and the LDS staging overlaps the HBM latency.
+template <int LAYOUT, int KS, int NSS, int RG, int MAXM, typename YT>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ scale,
     const uint8_t *__restrict__ packed, const float *__restrict__ gamma_p, int M, int64_t N,
     int64_t K, int64_t rb, YT *__restrict__ y, int32_t *__restrict__ acc_out) {
     using C = SkinnyCfg<LAYOUT>;
+    constexpr int kThreads = 64 * KS;
     constexpr int kRoundUnits = KS * NSS * 4;                 // units per round
     constexpr int kRoundK = kRoundUnits * C::kUnitCodes;       // codes per round
     constexpr int kActStride = kRoundK + 16;                   // LDS row stride (bytes)
+    constexpr int kChunksPerTok = kRoundK / 16;
+    constexpr int kMaxQ = (MAXM * kChunksPerTok + kThreads - 1) / kThreads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem);                 // base-3 only
     int8_t *act = reinterpret_cast<int8_t *>(smem + (LAYOUT == kLayoutBase3 ? 8192 : 0));
@@ -70,59 +111,93 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
 
     const int wave = threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
-    const int r = lane % 16;  // weight row within the block (A) / token (B)
+    const int r = lane % 16;  // weight row within a row group (A) / token (B)
     const int g = lane / 16;  // lane group = unit within the super-step
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
+    const float gamma = gamma_p[0];
 
-    if (LAYOUT == kLayoutBase3) {
-        for (int i = threadIdx.x; i < 4 * 256; i += 64 * KS)
+    if (LAYOUT == kLayoutBase3) {  // visible after the first round's barriers
+        for (int i = threadIdx.x; i < 4 * 256; i += kThreads)
             lut[i] = base3_entry((uint32_t)(i % 256)) << (8 * (i / 256));
     }
 
     const int64_t units = rb / 16;
-    const bool row_ok = n0 + r < N;
-    const uint8_t *wrow = packed + (n0 + r) * rb;
     const bool aligned = (K % 16) == 0;
-
-    v4i acc = {0, 0, 0, 0};
-    for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
-        // 1. issue every weight load of this round
-        uint4 wv[NSS];
+    const int chunks = M * kChunksPerTok;
+    const uint8_t *wrow[RG];
+    bool row_ok[RG];
 #pragma unroll
-        for (int s = 0; s < NSS; ++s) {
-            const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
-            const bool ok = row_ok && unit < units;
-            // out-of-range lanes read a valid address and are zeroed (no branch)
-            const uint4 v = *reinterpret_cast<const uint4 *>(ok ? wrow + unit * 16 : packed);
-            wv[s] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
-        // 2. stage activations xq[0:M, k0 : k0 + kRoundK] in LDS (zero past K)
+    for (int q = 0; q < RG; ++q) {
+        row_ok[q] = n0 + 16 * q + r < N;
+        wrow[q] = packed + (n0 + 16 * q + r) * rb;
+    }
+
+    v4i acc[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) acc[q] = v4i{0, 0, 0, 0};
+    for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
         const int64_t k0 = u0 * C::kUnitCodes;
-        __syncthreads();  // previous round's readers are done
-        const int chunks = M * (kRoundK / 16);
-        for (int q = threadIdx.x; q < chunks; q += 64 * KS) {
-            const int t = q / (kRoundK / 16), cc = q % (kRoundK / 16);
-            const int64_t k = k0 + cc * 16;
-            const int8_t *src = xq + (int64_t)t * K;
-            v4i v = {0, 0, 0, 0};
-            if (aligned) {
-                const bool ok = k < K;  // K % 16 == 0: a chunk is all in or all out
-                const v4i a = *reinterpret_cast<const v4i *>(ok ? src + k : xq);
-                v = ok ? a : v4i{0, 0, 0, 0};
-            } else if (k < K) {
+        // 1. this thread's chunks of xq[0:M, k0 : k0 + kRoundK] (16 bytes each;
+        //    with K % 16 == 0 a chunk is entirely inside or outside the row)
+        //    Out-of-range pieces (activations and weights alike) load a valid
+        //    address unconditionally and are zeroed where they are consumed: a
+        //    select right at the load would make the compiler wait for it there.
+        v4i xa[kMaxQ];
+        bool xok[kMaxQ];
+        if (aligned) {
+#pragma unroll
+            for (int i = 0; i < kMaxQ; ++i) {
+                const int q = threadIdx.x + i * kThreads;
+                const int t = q / kChunksPerTok;
+                const int64_t k = k0 + (q % kChunksPerTok) * 16;
+                xok[i] = q < chunks && k < K;
+                xa[i] = *reinterpret_cast<const v4i *>(xok[i] ? xq + (int64_t)t * K + k : xq);
+            }
+        }
+        // 2. every weight load of this round
+        uint4 wv[RG][NSS];
+        bool wok[RG][NSS];
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+#pragma unroll
+            for (int s = 0; s < NSS; ++s) {
+                const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
+                wok[q][s] = row_ok[q] && unit < units;
+                wv[q][s] =
+                    *reinterpret_cast<const uint4 *>(wok[q][s] ? wrow[q] + unit * 16 : packed);
+            }
+        // 3. stage the activations in LDS (zero past K)
+        lds_barrier();  // previous round's readers are done
+        if (aligned) {
+#pragma unroll
+            for (int i = 0; i < kMaxQ; ++i) {
+                const int q = threadIdx.x + i * kThreads;
+                if (q < chunks)
+                    *reinterpret_cast<v4i *>(act + (q / kChunksPerTok) * kActStride +
+                                             (q % kChunksPerTok) * 16) =
+                        xok[i] ? xa[i] : v4i{0, 0, 0, 0};
+            }
+        } else {
+            for (int q = threadIdx.x; q < chunks; q += kThreads) {
+                const int t = q / kChunksPerTok, cc = q % kChunksPerTok;
+                const int64_t k = k0 + cc * 16;
+                const int8_t *src = xq + (int64_t)t * K;
                 uint32_t d[4] = {0u, 0u, 0u, 0u};
                 for (int e = 0; e < 16; ++e)
                     if (k + e < K) d[e / 4] |= (uint32_t)(uint8_t)src[k + e] << (8 * (e % 4));
-                v = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+                *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) =
+                    v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
             }
-            *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) = v;
         }
-        __syncthreads();
-        // 3. expand and multiply
+        lds_barrier();
+        // 4. expand and multiply; one activation read feeds RG instructions
 #pragma unroll
         for (int s = 0; s < NSS; ++s) {
-            int c[20];
-            decode_unit<LAYOUT>(wv[s], lut, c);
+            int c[RG][20];
+#pragma unroll
+            for (int q = 0; q < RG; ++q)
+                decode_unit<LAYOUT>(wok[q][s] ? wv[q][s] : make_uint4(0u, 0u, 0u, 0u), lut,
+                                    c[q]);
             const int ul = (s * KS + wave) * 4 + g;  // unit within the round
 #pragma unroll
             for (int st = 0; st < C::kSteps; ++st) {
@@ -130,49 +205,54 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
                 if (r < M)
                     b = *reinterpret_cast<const v4i *>(act + r * kActStride +
                                                        ul * C::kUnitCodes + 16 * st);
-                const v4i a = {c[4 * st], c[4 * st + 1], c[4 * st + 2], c[4 * st + 3]};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < RG; ++q) {
+                    const v4i a = {c[q][4 * st], c[q][4 * st + 1], c[q][4 * st + 2],
+                                   c[q][4 * st + 3]};
+                    acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[q], 0, 0, 0);
+                }
             }
         }
     }
 
-    __syncthreads();
-    part[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    v4i tot = part[lane];
+    lds_barrier();
 #pragma unroll
-    for (int w = 1; w < KS; ++w) tot += part[w * 64 + lane];
-
-    // lane holds D[4g + i][r]: weight rows n0 + 4g + i, token r
+    for (int q = 0; q < RG; ++q) part[(q * KS + wave) * 64 + lane] = acc[q];
+    lds_barrier();
     const int t = r;
-    if (t >= M) return;
-    const float f = gamma_p[0] * scale[t] / 127.0f;
+    const float f = t < M ? gamma * scale[t] / 127.0f : 0.f;
+    for (int q = wave; q < RG; q += KS) {  // wave q finishes row group q
+        v4i tot = part[(q * KS) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t n = n0 + 4 * g + i;
-        if (n >= N) continue;
-        const int32_t a = tot[i];
-        const float v = (float)a * f;
-        if constexpr (sizeof(YT) == 4)
-            y[(int64_t)t * N + n] = v;
-        else
-            y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
-        if (acc_out) acc_out[(int64_t)t * N + n] = a;
+        for (int w = 1; w < KS; ++w) tot += part[(q * KS + w) * 64 + lane];
+        // lane holds D[4g + i][r]: weight rows n0 + 16q + 4g + i, token r
+        if (t >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = n0 + 16 * q + 4 * g + i;
+            if (n >= N) continue;
+            const int32_t a = tot[i];
+            const float v = (float)a * f;
+            if constexpr (sizeof(YT) == 4)
+                y[(int64_t)t * N + n] = v;
+            else
+                y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
+            if (acc_out) acc_out[(int64_t)t * N + n] = a;
+        }
     }
 }
 
-template <int LAYOUT, int KS, int NSS, typename YT>
+template <int LAYOUT, int KS, int NSS, int RG, int MAXM, typename YT>
 hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *packed,
                            const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int32_t *acc, hipStream_t s) {
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
-    // the partial-tile buffer aliases the activation area (needs KS*1 KiB)
+    // the partial-tile buffer aliases the activation area (needs KS*RG KiB)
     const size_t act = (size_t)M * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
-    const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) +
-                        (act > (size_t)KS * 1024 ? act : (size_t)KS * 1024);
-    dim3 grid((unsigned)((N + 15) / 16)), block(64 * KS);
-    auto kern = skinny_kernel<LAYOUT, KS, NSS, YT>;
+    const size_t part = (size_t)KS * RG * 1024;
+    const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (act > part ? act : part);
+    dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG))), block(64 * KS);
+    auto kern = skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, YT>;
     static int lds_raised = 0;  // one flag per instantiation of this launcher
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
@@ -185,19 +265,26 @@ template <int LAYOUT, typename YT>
 hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *packed,
                            const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int32_t *acc, hipStream_t s) {
-    // one round of 4 waves x 4 super-steps covers 4096 codes (2-bit) / 5120
-    // (base-3): 64 (80) KiB of activations at M = 16
-    return launch_skinny_t<LAYOUT, 4, 4, YT>(xq, scale, packed, gamma, M, N, K, y, acc, s);
+    // eight waves x two super-steps: one round covers 4096 codes (2-bit) or
+    // 5120 (base-3); at M = 16 that is 64 (80) KiB of staged activations
+    if (M <= 4)
+        return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 1, 4, YT>(xq, scale, packed, gamma, M, N, K,
+                                                               y, acc, s);
+    if (N >= kSkRG2MinN)
+        return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 2, 16, YT>(xq, scale, packed, gamma, M, N, K,
+                                                               y, acc, s);
+    return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 1, 16, YT>(xq, scale, packed, gamma, M, N, K,
+                                                           y, acc, s);
 }
 
 // ---------------------------------------------------------------------------
 // Fused decode (1 <= M <= 4 tokens): per-token absmax INT8 quantisation of x
 // inside every block, then the same weight-streaming product. Each block
-// issues its weight loads first, derives the token scales s_m = max(max|x|,
-// 1e-6) from a full pass over x (from L2), quantises the round's slice of x
-// straight into LDS with quant1() (the same fp32 steps as the stand-alone
-// quantiser, so codes are identical), and multiplies. One launch instead of
-// two on the latency-bound decode path.
+// loads its chunks of x (from L2), issues its weight loads, derives the token
+// scales s_m = max(max|x|, 1e-6) and quantises the round's slice of x into
+// LDS with quant1() (the same fp32 steps as the stand-alone quantiser, so
+// codes are identical) while the weights are still in flight, then
+// multiplies. One launch instead of two on the latency-bound decode path.
 constexpr int kFusedMaxM = 4;
 
 template <int LAYOUT, int KS, int NSS, int MAXM, typename XT, typename YT>
@@ -227,18 +314,49 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const uint8_t *wrow = packed + (n0 + r) * rb;
     const bool vec = (K % 8) == 0;
 
+    const float gamma = gamma_p[0];
     uint4 wv[NSS];
+    bool wok[NSS];
     auto issue = [&](int64_t u0) {
 #pragma unroll
         for (int s = 0; s < NSS; ++s) {
             const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
-            const bool ok = row_ok && unit < units;
-            // out-of-range lanes read a valid address and are zeroed
-            const uint8_t *src = ok ? wrow + unit * 16 : packed;
-            const uint4 v = *reinterpret_cast<const uint4 *>(src);
-            wv[s] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+            wok[s] = row_ok && unit < units;
+            // out-of-range lanes read a valid address; the value is zeroed
+            // where it is consumed, so no wait is forced here
+            wv[s] = *reinterpret_cast<const uint4 *>(wok[s] ? wrow + unit * 16 : packed);
         }
     };
+
+    // token scales: s_m = max(max_k |x[m, k]|, 1e-6), a block-wide max per
+    // token. When the row fits one round, each thread loads its 16-element
+    // chunks of x once and keeps them for the quantisation below. With
+    // K % 16 == 0 those loads are issued before the weight loads: memory
+    // counters complete in issue order, so the scale and quantisation work
+    // then overlaps the weights' HBM latency instead of following it.
+    constexpr int kChunksPerTok = kRoundK / 16;
+    constexpr int kMaxQ = (MAXM * kChunksPerTok + kThreads - 1) / kThreads;
+    constexpr int kRaw = (int)sizeof(XT);  // 16-byte pieces per 16-element chunk
+    const bool one_round = units <= kRoundUnits;
+    const bool early = one_round && (K % 16) == 0;
+    // (out-of-range chunks load a valid address unconditionally and are
+    // zeroed only after the weight loads are issued: a select right at the
+    // load would make the compiler wait for it there)
+    uint4 xr[kMaxQ][kRaw];
+    bool xok[kMaxQ];
+    if (early) {
+#pragma unroll
+        for (int i = 0; i < kMaxQ; ++i) {
+            const int q = threadIdx.x + i * kThreads;
+            const int t = q / kChunksPerTok;
+            const int64_t k = (int64_t)(q % kChunksPerTok) * 16;
+            xok[i] = t < M && k < K;
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(xok[i] ? x + (int64_t)t * K + k : x);
+#pragma unroll
+            for (int j = 0; j < kRaw; ++j) xr[i][j] = src[j];
+        }
+    }
     issue(0);
 
     if (LAYOUT == kLayoutBase3) {
@@ -246,12 +364,6 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
             lut[i] = base3_entry((uint32_t)(i % 256)) << (8 * (i / 256));
     }
 
-    // token scales: s_m = max(max_k |x[m, k]|, 1e-6), a block-wide max per
-    // token. When the row fits one round, each thread loads its 16-element
-    // chunks of x once and keeps them for the quantisation below.
-    constexpr int kChunksPerTok = kRoundK / 16;
-    constexpr int kMaxQ = (MAXM * kChunksPerTok + kThreads - 1) / kThreads;
-    const bool one_round = units <= kRoundUnits;
     float xv[kMaxQ][16];
     float amax[kFusedMaxM] = {0.f, 0.f, 0.f, 0.f};
     auto load_chunk = [&](int t, int64_t k, float *v) {
@@ -264,19 +376,31 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
             for (int e = 0; e < 16; ++e) v[e] = k + e < K ? Elem<XT>::get(row, k + e) : 0.f;
         }
     };
-    if (one_round) {
+    auto track_max = [&](int t, const float *v) {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxM; ++tt) amax[tt] = tt == t ? fmaxf(amax[tt], m) : amax[tt];
+    };
+    if (early) {
+#pragma unroll
+        for (int i = 0; i < kMaxQ; ++i) {
+            const int q = threadIdx.x + i * kThreads;
+            const int t = q / kChunksPerTok;
+            unpack_raw(xr[i], xv[i]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) xv[i][e] = xok[i] ? xv[i][e] : 0.f;
+            if (t < M) track_max(t, xv[i]);
+        }
+    } else if (one_round) {
 #pragma unroll
         for (int i = 0; i < kMaxQ; ++i) {
             const int q = threadIdx.x + i * kThreads;
             const int t = q / kChunksPerTok;
             if (t < M) {
                 load_chunk(t, (int64_t)(q % kChunksPerTok) * 16, xv[i]);
-                float m = 0.f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(xv[i][e]));
-#pragma unroll
-                for (int tt = 0; tt < kFusedMaxM; ++tt)
-                    amax[tt] = tt == t ? fmaxf(amax[tt], m) : amax[tt];
+                track_max(t, xv[i]);
             }
         }
     } else {
@@ -304,14 +428,14 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         const float m = wave_max(amax[t]);
         if (lane == 0) red[t][wave] = m;
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < M) {
         float m = red[threadIdx.x][0];
 #pragma unroll
         for (int w = 1; w < KS; ++w) m = fmaxf(m, red[threadIdx.x][w]);
         tok_scale[threadIdx.x] = fmaxf(m, 1e-6f);
     }
-    __syncthreads();
+    lds_barrier();
 
     auto store_codes = [&](int t, int cc, const float *v) {
         const float sc = tok_scale[t];
@@ -327,7 +451,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
         if (u0 > 0) {
             issue(u0);
-            __syncthreads();  // previous round's readers are done
+            lds_barrier();  // previous round's readers are done
         }
         // quantise x[0:M, k0 : k0 + kRoundK] into LDS (zero past K)
         const int64_t k0 = u0 * C::kUnitCodes;
@@ -345,11 +469,11 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
                 store_codes(t, cc, v);
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int s = 0; s < NSS; ++s) {
             int c[20];
-            decode_unit<LAYOUT>(wv[s], lut, c);
+            decode_unit<LAYOUT>(wok[s] ? wv[s] : make_uint4(0u, 0u, 0u, 0u), lut, c);
             const int ul = (s * KS + wave) * 4 + g;
 #pragma unroll
             for (int st = 0; st < C::kSteps; ++st) {
@@ -363,16 +487,16 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         }
     }
 
-    __syncthreads();
+    lds_barrier();
     part[wave * 64 + lane] = acc;
-    __syncthreads();
+    lds_barrier();
     if (wave != 0) return;
     v4i tot = part[lane];
 #pragma unroll
     for (int w = 1; w < KS; ++w) tot += part[w * 64 + lane];
     const int t = r;
     if (t >= M) return;
-    const float f = gamma_p[0] * tok_scale[t] / 127.0f;
+    const float f = gamma * tok_scale[t] / 127.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t n = n0 + 4 * g + i;
@@ -390,7 +514,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
 template <int LAYOUT, int MAXM, typename XT, typename YT>
 hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const float *gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
-    constexpr int KS = 4, NSS = 4;
+    constexpr int KS = kFdKS, NSS = kFdNSS;
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
     const size_t act = (size_t)MAXM * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) +
