@@ -145,6 +145,34 @@ bl_status bitlinear_linear(const void *x, int x_dtype, const uint8_t *packed, in
                            const float *gamma, int64_t M, int64_t N, int64_t K,
                            void *y, int y_dtype, int32_t *acc, void *stream);
 
+/* Backward products of the straight-through estimator, for training with the
+ * codes the forward pass used ([QAT-en] "How Gradients Flow: Fake Quantization
+ * and STE": the backward pass treats rounding as the identity, so gradients
+ * reach the latent weights; [b158] §5.3, the BitLinear layer with the
+ * straight-through estimator). With y = x W_q^T and W_q = gamma * c:
+ *   grad_x = grad_y W_q   and   grad_W = grad_y^T x.
+ * Both run on the bf16 matrix cores with fp32 accumulation.
+ *
+ * bitlinear_backward_input: grad_x[m,k] = gamma * sum_n grad_y[m,n] * c[n,k].
+ *   grad_y  [M, N] bf16 (gy_dtype must be BL_BF16).
+ *   packed  [N, row_bytes] codes in BL_PACK_2BIT (the forward's own matrix; no
+ *           transposed copy is needed); gamma: 1 float (device).
+ *   grad_x  out: [M, K] fp32.
+ * Requires N % 8 == 0. BL_F32 grad_y, BL_PACK_BASE3 or other N return
+ * BL_ERR_UNSUPPORTED. Dimensions above 2^24 return BL_ERR_INVALID_ARG.
+ * M = 0 is a no-op; N = 0 writes zeros. */
+bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,
+                                   int layout, const float *gamma, int64_t M, int64_t N,
+                                   int64_t K, float *grad_x, void *stream);
+
+/* bitlinear_backward_weight: grad_w[n,k] = sum_m grad_y[m,n] * x[m,k].
+ *   grad_y  [M, N] bf16; x [M, K] bf16 (the layer input; dtype must be BL_BF16).
+ *   grad_w  out: [N, K] fp32.
+ * Requires N % 8 == 0 and K % 8 == 0 (else BL_ERR_UNSUPPORTED). N = 0 is a
+ * no-op; M = 0 writes zeros. */
+bl_status bitlinear_backward_weight(const void *grad_y, const void *x, int dtype, int64_t M,
+                                    int64_t N, int64_t K, float *grad_w, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *bitlinear_status_string(int status);
 

@@ -6,8 +6,9 @@ There is no CPU or PyTorch fallback: if the library is missing, importing
 this module raises.
 
 Functions keep the C names (``bitlinear_pack_weights``,
-``bitlinear_quant_acts``, ``bitlinear_forward``) and take torch tensors;
-``linear`` chains activation quantisation and the forward product.
+``bitlinear_quant_acts``, ``bitlinear_forward``, ``bitlinear_linear``,
+``bitlinear_backward_input``, ``bitlinear_backward_weight``) and take torch
+tensors; ``linear`` chains activation quantisation and the forward product.
 """
 from __future__ import annotations
 
@@ -47,6 +48,10 @@ _lib.bitlinear_forward.restype = _int
 _lib.bitlinear_forward.argtypes = [_p, _p, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
 _lib.bitlinear_linear.restype = _int
 _lib.bitlinear_linear.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
+_lib.bitlinear_backward_input.restype = _int
+_lib.bitlinear_backward_input.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _p]
+_lib.bitlinear_backward_weight.restype = _int
+_lib.bitlinear_backward_weight.argtypes = [_p, _p, _int, _i64, _i64, _i64, _p, _p]
 _lib.bitlinear_status_string.restype = ctypes.c_char_p
 _lib.bitlinear_status_string.argtypes = [_int]
 _lib.bitlinear_version.restype = _int
@@ -54,7 +59,8 @@ _lib.bitlinear_version.argtypes = []
 
 EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
             "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
-            "bitlinear_linear", "bitlinear_status_string", "bitlinear_version"]
+            "bitlinear_linear", "bitlinear_backward_input", "bitlinear_backward_weight",
+            "bitlinear_status_string", "bitlinear_version"]
 FUSED_MAX_M = 4
 
 
@@ -179,6 +185,35 @@ def bitlinear_linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor,
                                  _ptr(acc) if want_acc else None, _stream(stream)),
            "bitlinear_linear")
     return (y, acc) if want_acc else y
+
+
+def bitlinear_backward_input(grad_y: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor,
+                             K: int, layout="2bit", grad_x: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    """grad_x [M, K] fp32 = gamma * grad_y [M, N] (bf16) x codes of packed [N, row_bytes]."""
+    assert grad_y.dim() == 2 and grad_y.is_contiguous() and grad_y.dtype in _DTYPES
+    M, N = grad_y.shape
+    if grad_x is None:
+        grad_x = torch.empty((M, K), dtype=torch.float32, device=grad_y.device)
+    _check(_lib.bitlinear_backward_input(_ptr(grad_y), _DTYPES[grad_y.dtype], _ptr(packed),
+                                         _layout(layout), _ptr(gamma), M, N, K, _ptr(grad_x),
+                                         _stream(stream)), "bitlinear_backward_input")
+    return grad_x
+
+
+def bitlinear_backward_weight(grad_y: torch.Tensor, x: torch.Tensor,
+                              grad_w: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """grad_w [N, K] fp32 = grad_y^T (bf16 [M, N]) x x (bf16 [M, K])."""
+    assert grad_y.dim() == 2 and x.dim() == 2 and grad_y.shape[0] == x.shape[0]
+    assert grad_y.is_contiguous() and x.is_contiguous() and grad_y.dtype == x.dtype
+    M, N = grad_y.shape
+    K = x.shape[1]
+    if grad_w is None:
+        grad_w = torch.empty((N, K), dtype=torch.float32, device=x.device)
+    _check(_lib.bitlinear_backward_weight(_ptr(grad_y), _ptr(x), _DTYPES[x.dtype], M, N, K,
+                                          _ptr(grad_w), _stream(stream)),
+           "bitlinear_backward_weight")
+    return grad_w
 
 
 def linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int, layout="2bit",

@@ -14,6 +14,9 @@ namespace {
 
 constexpr int64_t kMaxK = 2147483647LL / 127;  // 127 * K must fit in INT32
 constexpr int kMaxDevices = 64;
+// Backward products: every dimension below 2^24 keeps tile counts and the
+// products of two dimensions far inside 64-bit indexing.
+constexpr int64_t kMaxDim = 1LL << 24;
 
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
 std::atomic<int> g_arch[kMaxDevices];
@@ -137,6 +140,43 @@ bl_status bitlinear_linear(const void *x, int x_dtype, const uint8_t *packed, in
     if (st != BL_OK) return st;
     return launched(bl::launch_linear_decode(x, x_dtype, packed, layout, gamma, M, N, K, y,
                                              y_dtype, acc, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,
+                                   int layout, const float *gamma, int64_t M, int64_t N,
+                                   int64_t K, float *grad_x, void *stream) {
+    if (!grad_y || !packed || !gamma || !grad_x) return BL_ERR_INVALID_ARG;
+    if (!aligned16(grad_y) || !aligned16(packed) || !aligned16(gamma) || !aligned16(grad_x))
+        return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(gy_dtype) || !valid_layout(layout)) return BL_ERR_INVALID_ARG;
+    if (gy_dtype != BL_BF16 || layout != BL_PACK_2BIT || N % 8 != 0) return BL_ERR_UNSUPPORTED;
+    if (M == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N == 0) return launched(bl::launch_zero_f32(grad_x, M * K, s));
+    return launched(bl::launch_backward_input(static_cast<const uint16_t *>(grad_y), packed, gamma,
+                                              M, N, K, grad_x, s));
+}
+
+bl_status bitlinear_backward_weight(const void *grad_y, const void *x, int dtype, int64_t M,
+                                    int64_t N, int64_t K, float *grad_w, void *stream) {
+    if (!grad_y || !x || !grad_w) return BL_ERR_INVALID_ARG;
+    if (!aligned16(grad_y) || !aligned16(x) || !aligned16(grad_w)) return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return BL_ERR_INVALID_ARG;
+    if (dtype != BL_BF16 || N % 8 != 0 || K % 8 != 0) return BL_ERR_UNSUPPORTED;
+    if (N == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 0) return launched(bl::launch_zero_f32(grad_w, N * K, s));
+    return launched(bl::launch_backward_weight(static_cast<const uint16_t *>(grad_y),
+                                               static_cast<const uint16_t *>(x), M, N, K, grad_w,
+                                               s));
 }
 
 const char *bitlinear_status_string(int status) {

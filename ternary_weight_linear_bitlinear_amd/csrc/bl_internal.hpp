@@ -64,4 +64,16 @@ hipError_t launch_forward_gemm(const int8_t *xq, const float *scale,
                                int64_t K, void *y, int y_dtype, int32_t *acc,
                                hipStream_t stream);
 
+
+// ---- backward products (backward.hip) ------------------------------------
+// grad_x [M, K] fp32 = gamma * grad_y [M, N] (bf16) x codes of packed [N, rb2(K)].
+hipError_t launch_backward_input(const uint16_t *grad_y, const uint8_t *packed,
+                                 const float *gamma, int64_t M, int64_t N, int64_t K,
+                                 float *grad_x, hipStream_t stream);
+// grad_w [N, K] fp32 = grad_y^T (bf16 [M, N]) x x (bf16 [M, K]).
+hipError_t launch_backward_weight(const uint16_t *grad_y, const uint16_t *x, int64_t M,
+                                  int64_t N, int64_t K, float *grad_w, hipStream_t stream);
+// out[0 : count) = 0 (a kernel, so it can be captured in a graph).
+hipError_t launch_zero_f32(float *out, int64_t count, hipStream_t stream);
+
 }  // namespace bl

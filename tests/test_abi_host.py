@@ -132,3 +132,39 @@ def test_fused_linear_rejects_and_limits(bl):
     assert f(layout=9) == bl.BL_ERR_INVALID_ARG
     assert f(M=5) == bl.BL_ERR_UNSUPPORTED  # fused path covers M <= 4 only
     assert f(M=0) == bl.BL_OK
+
+
+def test_backward_rejects_and_limits(bl):
+    lib = bl.library()
+    bi = lambda **kw: lib.bitlinear_backward_input(kw.get("gy", P), kw.get("dt", 1), P,
+                                                   kw.get("layout", 0), kw.get("gamma", P),
+                                                   kw.get("M", 4), kw.get("N", 64),
+                                                   kw.get("K", 64), kw.get("gx", P), None)
+    assert bi(gy=None) == bl.BL_ERR_INVALID_ARG
+    assert bi(gamma=None) == bl.BL_ERR_INVALID_ARG
+    assert bi(gx=P + 4) == bl.BL_ERR_INVALID_ARG
+    assert bi(K=0) == bl.BL_ERR_INVALID_ARG
+    assert bi(M=-1) == bl.BL_ERR_INVALID_ARG
+    assert bi(N=(1 << 24) + 8) == bl.BL_ERR_INVALID_ARG
+    assert bi(dt=5) == bl.BL_ERR_INVALID_ARG
+    assert bi(layout=4) == bl.BL_ERR_INVALID_ARG
+    assert bi(dt=0) == bl.BL_ERR_UNSUPPORTED       # fp32 grad_y
+    assert bi(layout=1) == bl.BL_ERR_UNSUPPORTED   # base-3 codes
+    assert bi(N=60) == bl.BL_ERR_UNSUPPORTED       # N % 8 != 0
+    assert bi(M=0) == bl.BL_OK
+    bw = lambda **kw: lib.bitlinear_backward_weight(kw.get("gy", P), kw.get("x", P),
+                                                    kw.get("dt", 1), kw.get("M", 4),
+                                                    kw.get("N", 64), kw.get("K", 64),
+                                                    kw.get("gw", P), None)
+    assert bw(x=None) == bl.BL_ERR_INVALID_ARG
+    assert bw(gw=P + 8) == bl.BL_ERR_INVALID_ARG
+    assert bw(K=0) == bl.BL_ERR_INVALID_ARG
+    assert bw(dt=3) == bl.BL_ERR_INVALID_ARG
+    assert bw(dt=0) == bl.BL_ERR_UNSUPPORTED
+    assert bw(K=60) == bl.BL_ERR_UNSUPPORTED
+    assert bw(N=12) == bl.BL_ERR_UNSUPPORTED
+    assert bw(N=0) == bl.BL_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert bi() == bl.BL_ERR_DEVICE
+        assert bw() == bl.BL_ERR_DEVICE
