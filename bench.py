@@ -12,8 +12,11 @@ Infinity Cache) so the weights come from HBM.
 The same run measures the other rows of the path and reports them under
 "rows": the base-3 layout of the decode GEMV, weight packing, activation
 quantisation at prefill size, the prefill GEMM (M = 2048, K = 4096,
-N = 11008, INT8 TOPS) and one transformer block's six BitLinear layers at
-decode batch 16 and prefill 512 (tokens/s).
+N = 11008, INT8 TOPS), one transformer block's six BitLinear layers at
+decode batch 16 and prefill 512 (tokens/s), the training step at
+M = K = N = 4096 (re-quantise, INT8 forward, bf16 straight-through backward
+products) and, for context, the same decode and prefill layers with dense
+bf16 weights through torch linear (hipBLASLt).
 
 Timing: every measured sequence is captured once into a HIP graph and
 replayed between two HIP events on the replay stream, so host-side launch
@@ -36,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5033.0        # dense INT8 MFMA: 256 CU x 4 SIMD x 2048 ops/clk x 2.4 GHz
+BF16_PEAK_TFLOPS = 2516.0      # dense bf16 MFMA: 256 CU x 4 SIMD x 1024 flops/clk x 2.4 GHz
 METRIC = "BitLinear weight GB/s (decode GEMV) + INT8 TOPS (prefill), % of roofline"
 
 
@@ -278,6 +282,93 @@ def main():
             del cps
             torch.cuda.empty_cache()
         rows["block_stack"] = blk
+
+    # -------------------------------------------------------- training step
+    # Latent bf16 weights are re-quantised every step (absmean + 2-bit pack),
+    # then activation quantisation, the INT8 forward GEMM and the two
+    # straight-through-estimator backward products on the bf16 matrix cores.
+    if want("train"):
+        log("training step: generating inputs")
+        t = synth.workload("train")
+        Wt = to_dev(t.w_store, True)
+        xt = to_dev(t.x_store, True)
+        gyt = to_dev(t.grad_y_store, True)
+        pk_t = torch.empty((t.N, bl.bitlinear_packed_row_bytes(t.K, "2bit")), dtype=torch.uint8,
+                           device=dev)
+        g_t = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+        ws_t = torch.empty(bl.bitlinear_pack_workspace_bytes(t.N, t.K), dtype=torch.uint8,
+                           device=dev)
+        xq_t = torch.empty((t.M, t.K), dtype=torch.int8, device=dev)
+        sc_t = torch.empty(t.M, dtype=torch.float32, device=dev)
+        y_t = torch.empty((t.M, t.N), dtype=torch.bfloat16, device=dev)
+        gx_t = torch.empty((t.M, t.K), dtype=torch.float32, device=dev)
+        gw_t = torch.empty((t.N, t.K), dtype=torch.float32, device=dev)
+        parts = {
+            "requant_pack": lambda i: bl.bitlinear_pack_weights(Wt, "2bit", packed=pk_t, gamma=g_t,
+                                                                workspace=ws_t),
+            "quant_acts": lambda i: bl.bitlinear_quant_acts(xt, xq=xq_t, scale=sc_t),
+            "forward_int8": lambda i: bl.bitlinear_forward(xq_t, sc_t, pk_t, g_t, t.N, t.K, "2bit",
+                                                           torch.bfloat16, y=y_t),
+            "backward_input_bf16": lambda i: bl.bitlinear_backward_input(gyt, pk_t, g_t, t.K,
+                                                                         grad_x=gx_t),
+            "backward_weight_bf16": lambda i: bl.bitlinear_backward_weight(gyt, xt, grad_w=gw_t),
+        }
+        flop = 2.0 * t.M * t.N * t.K
+        tr = {}
+        for name, f in parts.items():
+            tr[name + "_ms"] = graph_ms(f, 10)
+
+        def train_step(i):
+            for f in parts.values():
+                f(i)
+
+        tr["step_ms"] = graph_ms(train_step, 10)
+        tr["forward_int8_tops"] = flop / (tr["forward_int8_ms"] * 1e-3) / 1e12
+        tr["forward_int8_frac"] = tr["forward_int8_tops"] / INT8_PEAK_TOPS
+        for name in ("backward_input_bf16", "backward_weight_bf16"):
+            tf = flop / (tr[name + "_ms"] * 1e-3) / 1e12
+            tr[name + "_tflops"] = tf
+            tr[name + "_frac"] = tf / BF16_PEAK_TFLOPS
+        tr["tokens_per_s"] = t.M / (tr["step_ms"] * 1e-3)
+        rows["train_step_4096"] = tr
+        log(f"training step: {tr['step_ms']*1e3:.0f} us/step (fwd {tr['forward_int8_ms']*1e3:.0f}, "
+            f"bwd in {tr['backward_input_bf16_ms']*1e3:.0f}, bwd w {tr['backward_weight_bf16_ms']*1e3:.0f} us)")
+        del Wt, xt, gyt, pk_t, xq_t, y_t, gx_t, gw_t
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------- bf16 comparison lines
+    # What a GPU without ternary kernels runs: the same layers with dense bf16
+    # weights through the vendor GEMM (torch linear -> hipBLASLt). Context for
+    # the ternary path's numbers, not part of the path.
+    if want("bf16_baseline"):
+        log("bf16 dense baseline (torch linear)")
+        base = {}
+        # weights [N, K] as a linear layer stores them (2-D products only)
+        F = torch.nn.functional
+        Wd = torch.randn((p.N, p.K), device=dev).mul_(0.02).to(torch.bfloat16)
+        nrot = 20  # 20 x 32 MiB: past the 256 MB Infinity Cache
+        wds = [Wd.clone() for _ in range(nrot)]
+        xd = xs[0]
+        ms = graph_ms(lambda i: F.linear(xd, wds[i % nrot]), 2 * nrot)
+        wb = p.N * p.K * 2
+        base["decode_gemv_bf16"] = dict(ms=ms, weight_bytes=wb, gbs=wb / (ms * 1e-3) / 1e9,
+                                        ternary_speedup=ms / decode["2bit"]["ms_per_step"])
+        log(f"bf16 decode GEMV: {ms*1e3:.2f} us ({wb/(ms*1e-3)/1e9:.0f} GB/s), ternary fused "
+            f"step is {base['decode_gemv_bf16']['ternary_speedup']:.2f}x faster")
+        del wds
+        q = synth.WORKLOADS["prefill"]
+        xb = torch.randn((q["M"], q["K"]), device=dev).to(torch.bfloat16)
+        Wb = torch.randn((q["N"], q["K"]), device=dev).mul_(0.02).to(torch.bfloat16)
+        ms = graph_ms(lambda i: F.linear(xb, Wb), 10)
+        ops = 2.0 * q["M"] * q["N"] * q["K"]
+        base["prefill_gemm_bf16"] = dict(ms=ms, tflops=ops / (ms * 1e-3) / 1e12,
+                                         frac=ops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+        if "prefill_gemm" in rows:
+            base["prefill_gemm_bf16"]["ternary_speedup"] = ms / rows["prefill_gemm"]["2bit"]["gemm_ms"]
+        log(f"bf16 prefill GEMM: {ms*1e3:.1f} us ({base['prefill_gemm_bf16']['tflops']:.0f} TFLOP/s)")
+        rows["bf16_dense_baseline"] = base
+        del xb, Wb
+        torch.cuda.empty_cache()
 
     # --------------------------------------------------------- CPU baseline
     cpu = None
