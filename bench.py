@@ -256,19 +256,29 @@ def main():
             pb = synth.block_layer(i, 1)
             packed, gamma = bl.bitlinear_pack_weights(to_dev(pb.w_store, True), "2bit")
             layers.append((name, N, K, packed, gamma))
+        # Q, K and V read the same input: stacked into one packed matrix with
+        # three gammas, they run as one launch
+        rb4 = layers[0][3].shape[1]
+        qkv = torch.empty((3 * 4096, rb4), dtype=torch.uint8, device=dev)
+        qkv_g = torch.zeros(4, dtype=torch.float32, device=dev)
+        for s_ in range(3):
+            qkv[s_ * 4096:(s_ + 1) * 4096].copy_(layers[s_][3])
+            qkv_g[s_:s_ + 1].copy_(layers[s_][4])
         blk = {}
         for M in (16, 512):
             ncopy = 16 if M == 16 else 1
             cps = [[(n, N, K, pk.clone() if c else pk, g) for (n, N, K, pk, g) in layers]
                    for c in range(ncopy)]
+            qkvs = [qkv.clone() if c else qkv for c in range(ncopy)]
             xin = {K: to_dev(synth.make_problem(M=M, N=1, K=K, seed=77 + K, dtype="bf16").x_store, True)
                    for K in (4096, 11008)}
             ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for (_, N, _, _, _) in layers]
+            y_qkv = torch.empty((M, 3 * 4096), dtype=torch.bfloat16, device=dev)
             qbuf = {K: (torch.empty((M, K), dtype=torch.int8, device=dev),
                         torch.empty(M, dtype=torch.float32, device=dev)) for K in (4096, 11008)}
 
-            def block(i, cps=cps, xin=xin, ys=ys, qbuf=qbuf):
-                # Q, K, V share one quantised input; O, up and down each quantise their own
+            def block_separate(i, cps=cps, xin=xin, ys=ys, qbuf=qbuf):
+                # six launches; Q, K, V share one quantised input
                 ls = cps[i % len(cps)]
                 for j, (_, N, K, pk, g) in enumerate(ls):
                     if j in (0, 3, 4, 5):
@@ -276,10 +286,27 @@ def main():
                     bl.bitlinear_forward(qbuf[K][0], qbuf[K][1], pk, g, N, K, "2bit",
                                          torch.bfloat16, y=ys[j])
 
-            ms = graph_ms(block, 32 if M == 16 else 8)
-            blk[f"M{M}"] = dict(ms_per_block=ms, tokens_per_s=M / (ms * 1e-3))
-            log(f"block M={M}: {ms*1e3:.1f} us/block, {M/(ms*1e-3):.3g} tok/s")
-            del cps
+            def block(i, cps=cps, qkvs=qkvs, xin=xin, ys=ys, qbuf=qbuf, y_qkv=y_qkv):
+                # Q|K|V stacked (one launch), then O, up and down
+                c = i % len(cps)
+                xq4, sc4 = qbuf[4096]
+                bl.bitlinear_quant_acts(xin[4096], xq=xq4, scale=sc4)
+                bl.bitlinear_forward_segmented(xq4, sc4, qkvs[c], qkv_g, (4096, 4096, 4096), 4096,
+                                               "2bit", torch.bfloat16, y=y_qkv)
+                for j in (3, 4, 5):
+                    _, N, K, pk, g = cps[c][j]
+                    bl.bitlinear_quant_acts(xin[K], xq=qbuf[K][0], scale=qbuf[K][1])
+                    bl.bitlinear_forward(qbuf[K][0], qbuf[K][1], pk, g, N, K, "2bit",
+                                         torch.bfloat16, y=ys[j])
+
+            n_rep = 32 if M == 16 else 8
+            ms = graph_ms(block, n_rep)
+            ms_sep = graph_ms(block_separate, n_rep)
+            blk[f"M{M}"] = dict(ms_per_block=ms, tokens_per_s=M / (ms * 1e-3),
+                                ms_per_block_six_launches=ms_sep)
+            log(f"block M={M}: {ms*1e3:.1f} us/block with Q|K|V stacked ({M/(ms*1e-3):.3g} tok/s), "
+                f"{ms_sep*1e3:.1f} us as six launches")
+            del cps, qkvs
             torch.cuda.empty_cache()
         rows["block_stack"] = blk
 

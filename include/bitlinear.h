@@ -17,12 +17,14 @@
  *    row-major (M tokens), y is [M, N] row-major: y = x W^T ([b158] §4.2,
  *    y_i = sum_j w_ij x_j).
  *  - Every array argument is a DEVICE pointer, owned and allocated by the
- *    caller, 16-byte aligned. The library never allocates, frees or
+ *    caller, 16-byte aligned, except the weight scales (gamma, gammas), which
+ *    need only 4-byte alignment so that a stack of matrices can keep its
+ *    scales in consecutive floats. The library never allocates, frees or
  *    synchronises: each call only enqueues kernels on `stream` (a hipStream_t
  *    passed as void*, NULL = the default stream) and returns.
  *  - Argument errors are detected before any HIP call; the call then returns
  *    BL_ERR_INVALID_ARG with no side effect. Bad arguments are: a NULL
- *    required pointer, a pointer not 16-byte aligned, a negative size, K < 1,
+ *    required pointer, a misaligned pointer, a negative size, K < 1,
  *    K > 16909320 (127*K must fit in INT32), an unknown dtype / layout /
  *    scheme, a too-small workspace. M = 0 or N = 0 is an empty problem and
  *    returns BL_OK without launching anything (pack_weights needs N >= 1).
@@ -144,6 +146,31 @@ bl_status bitlinear_forward(const int8_t *xq, const float *scale,
 bl_status bitlinear_linear(const void *x, int x_dtype, const uint8_t *packed, int layout,
                            const float *gamma, int64_t M, int64_t N, int64_t K,
                            void *y, int y_dtype, int32_t *acc, void *stream);
+
+/* Stacked matrices: several weight matrices that share an input (the Q, K and
+ * V projections of an attention block) stored as consecutive row segments of
+ * one packed matrix, each segment quantised on its own with its own gamma, so
+ * one launch serves all of them (launch latency dominates the decode regime).
+ * Per segment the result is exactly that of bitlinear_forward /
+ * bitlinear_linear on the segment alone; y holds the segments' outputs side by
+ * side along its columns.
+ *   packed    [N, row_bytes] with N = sum(seg_rows): segment s occupies the
+ *             seg_rows[s] rows after segments 0..s-1 (pack each segment with
+ *             bitlinear_pack_weights into its row range, and its gamma into
+ *             gammas + s).
+ *   gammas    device array of nseg floats.
+ *   seg_rows  HOST array of nseg row counts, each >= 1; 1 <= nseg <= 8.
+ *   y, acc    [M, N].
+ * Other arguments, limits and errors as for bitlinear_forward /
+ * bitlinear_linear; a bad segment table returns BL_ERR_INVALID_ARG. */
+bl_status bitlinear_forward_segmented(const int8_t *xq, const float *scale, const uint8_t *packed,
+                                      int layout, const float *gammas, const int64_t *seg_rows,
+                                      int nseg, int64_t M, int64_t K, void *y, int y_dtype,
+                                      int32_t *acc, void *stream);
+bl_status bitlinear_linear_segmented(const void *x, int x_dtype, const uint8_t *packed, int layout,
+                                     const float *gammas, const int64_t *seg_rows, int nseg,
+                                     int64_t M, int64_t K, void *y, int y_dtype, int32_t *acc,
+                                     void *stream);
 
 /* Backward products of the straight-through estimator, for training with the
  * codes the forward pass used ([QAT-en] "How Gradients Flow: Fake Quantization

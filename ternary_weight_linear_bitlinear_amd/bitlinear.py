@@ -48,6 +48,12 @@ _lib.bitlinear_forward.restype = _int
 _lib.bitlinear_forward.argtypes = [_p, _p, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
 _lib.bitlinear_linear.restype = _int
 _lib.bitlinear_linear.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
+_lib.bitlinear_forward_segmented.restype = _int
+_lib.bitlinear_forward_segmented.argtypes = [_p, _p, _p, _int, _p, _p, _int, _i64, _i64, _p, _int,
+                                             _p, _p]
+_lib.bitlinear_linear_segmented.restype = _int
+_lib.bitlinear_linear_segmented.argtypes = [_p, _int, _p, _int, _p, _p, _int, _i64, _i64, _p, _int,
+                                            _p, _p]
 _lib.bitlinear_backward_input.restype = _int
 _lib.bitlinear_backward_input.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _p]
 _lib.bitlinear_backward_weight.restype = _int
@@ -59,7 +65,8 @@ _lib.bitlinear_version.argtypes = []
 
 EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
             "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
-            "bitlinear_linear", "bitlinear_backward_input", "bitlinear_backward_weight",
+            "bitlinear_linear", "bitlinear_forward_segmented", "bitlinear_linear_segmented",
+            "bitlinear_backward_input", "bitlinear_backward_weight",
             "bitlinear_status_string", "bitlinear_version"]
 FUSED_MAX_M = 4
 
@@ -184,6 +191,52 @@ def bitlinear_linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor,
                                  _ptr(gamma), M, N, K, _ptr(y), _DTYPES[y.dtype],
                                  _ptr(acc) if want_acc else None, _stream(stream)),
            "bitlinear_linear")
+    return (y, acc) if want_acc else y
+
+
+def _seg_table(seg_rows):
+    rows = [int(r) for r in seg_rows]
+    return (ctypes.c_int64 * len(rows))(*rows), len(rows), sum(rows)
+
+
+def bitlinear_forward_segmented(xq: torch.Tensor, scale: torch.Tensor, packed: torch.Tensor,
+                                gammas: torch.Tensor, seg_rows, K: int, layout="2bit",
+                                out_dtype=torch.float32, y: torch.Tensor | None = None,
+                                acc: torch.Tensor | bool | None = None, stream=None):
+    """bitlinear_forward over a stack of row segments, each with its own gamma
+    (gammas[s]); y [M, sum(seg_rows)]."""
+    M = xq.shape[0]
+    table, nseg, N = _seg_table(seg_rows)
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    want_acc = acc is not None and acc is not False
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _check(_lib.bitlinear_forward_segmented(_ptr(xq), _ptr(scale), _ptr(packed), _layout(layout),
+                                            _ptr(gammas), table, nseg, M, K, _ptr(y),
+                                            _DTYPES[y.dtype], _ptr(acc) if want_acc else None,
+                                            _stream(stream)), "bitlinear_forward_segmented")
+    return (y, acc) if want_acc else y
+
+
+def bitlinear_linear_segmented(x: torch.Tensor, packed: torch.Tensor, gammas: torch.Tensor,
+                               seg_rows, layout="2bit", out_dtype=torch.float32,
+                               y: torch.Tensor | None = None,
+                               acc: torch.Tensor | bool | None = None, stream=None):
+    """Fused quantise + multiply (M <= 4) over a stack of row segments."""
+    assert x.dim() == 2 and x.is_contiguous() and x.dtype in _DTYPES
+    M, K = x.shape
+    table, nseg, N = _seg_table(seg_rows)
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    want_acc = acc is not None and acc is not False
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    _check(_lib.bitlinear_linear_segmented(_ptr(x), _DTYPES[x.dtype], _ptr(packed),
+                                           _layout(layout), _ptr(gammas), table, nseg, M, K,
+                                           _ptr(y), _DTYPES[y.dtype],
+                                           _ptr(acc) if want_acc else None, _stream(stream)),
+           "bitlinear_linear_segmented")
     return (y, acc) if want_acc else y
 
 

@@ -22,6 +22,7 @@ constexpr int64_t kMaxDim = 1LL << 24;
 std::atomic<int> g_arch[kMaxDevices];
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool valid_dtype(int d) { return d == BL_F32 || d == BL_BF16; }
 bool valid_layout(int l) { return l == BL_PACK_2BIT || l == BL_PACK_BASE3; }
 bool valid_scheme(int s) { return s == BL_TERNARY || s == BL_BINARY; }
@@ -57,6 +58,61 @@ int64_t row_bytes(int64_t K, int layout) {
     return layout == BL_PACK_2BIT ? bl::row_bytes_2bit(K) : bl::row_bytes_base3(K);
 }
 
+// Segment table of a stacked matrix: 1..kMaxSegments host row counts, each
+// >= 1. Fills `gm` (bounds = running row totals) and `N` (the total).
+bool make_segments(const float *gammas, const int64_t *seg_rows, int nseg, bl::GammaMap &gm,
+                   int64_t &N) {
+    if (!seg_rows || nseg < 1 || nseg > bl::kMaxSegments) return false;
+    gm = bl::GammaMap::single(gammas);
+    gm.nseg = nseg;
+    N = 0;
+    for (int s = 0; s < nseg; ++s) {
+        if (seg_rows[s] < 1 || seg_rows[s] > 2147483647LL - N) return false;
+        N += seg_rows[s];
+        if (s + 1 < nseg) gm.bound[s] = N;
+    }
+    return true;
+}
+
+bl_status forward_impl(const int8_t *xq, const float *scale, const uint8_t *packed, int layout,
+                       const float *gamma, const bl::GammaMap &gm, int64_t M, int64_t N,
+                       int64_t K, void *y, int y_dtype, int32_t *acc, void *stream) {
+    if (!xq || !scale || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(scale) || !aligned16(packed) || !aligned4(gamma) ||
+        !aligned16(y) || (acc && !aligned16(acc)))
+        return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || K > kMaxK) return BL_ERR_INVALID_ARG;
+    if (M > 65535LL * 128 || N > 2147483647LL) return BL_ERR_INVALID_ARG;
+    if (!valid_layout(layout) || !valid_dtype(y_dtype)) return BL_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M <= bl::kSkinnyMaxM)
+        return launched(
+            bl::launch_forward_skinny(xq, scale, packed, layout, gm, M, N, K, y, y_dtype, acc, s));
+    return launched(
+        bl::launch_forward_gemm(xq, scale, packed, layout, gm, M, N, K, y, y_dtype, acc, s));
+}
+
+bl_status linear_impl(const void *x, int x_dtype, const uint8_t *packed, int layout,
+                      const float *gamma, const bl::GammaMap &gm, int64_t M, int64_t N, int64_t K,
+                      void *y, int y_dtype, int32_t *acc, void *stream) {
+    if (!x || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(packed) || !aligned4(gamma) || !aligned16(y) ||
+        (acc && !aligned16(acc)))
+        return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || K > kMaxK || N > 2147483647LL) return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(x_dtype) || !valid_layout(layout) || !valid_dtype(y_dtype))
+        return BL_ERR_INVALID_ARG;
+    if (M > bl::fused_decode_max_m()) return BL_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    return launched(bl::launch_linear_decode(x, x_dtype, packed, layout, gm, M, N, K, y, y_dtype,
+                                             acc, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,7 +131,7 @@ bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t 
                                  int layout, float eps, uint8_t *packed, float *gamma,
                                  void *workspace, size_t workspace_bytes, void *stream) {
     if (!W || !packed || !gamma || !workspace) return BL_ERR_INVALID_ARG;
-    if (!aligned16(W) || !aligned16(packed) || !aligned16(gamma) || !aligned16(workspace))
+    if (!aligned16(W) || !aligned16(packed) || !aligned4(gamma) || !aligned16(workspace))
         return BL_ERR_INVALID_ARG;
     if (N < 1 || K < 1 || K > kMaxK) return BL_ERR_INVALID_ARG;
     if (N > INT64_MAX / K) return BL_ERR_INVALID_ARG;
@@ -106,47 +162,42 @@ bl_status bitlinear_quant_acts(const void *x, int x_dtype, int64_t M, int64_t K,
 bl_status bitlinear_forward(const int8_t *xq, const float *scale, const uint8_t *packed,
                             int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                             void *y, int y_dtype, int32_t *acc, void *stream) {
-    if (!xq || !scale || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
-    if (!aligned16(xq) || !aligned16(scale) || !aligned16(packed) || !aligned16(gamma) ||
-        !aligned16(y) || (acc && !aligned16(acc)))
-        return BL_ERR_INVALID_ARG;
-    if (M < 0 || N < 0 || K < 1 || K > kMaxK) return BL_ERR_INVALID_ARG;
-    if (M > 65535LL * 128 || N > 2147483647LL) return BL_ERR_INVALID_ARG;
-    if (!valid_layout(layout) || !valid_dtype(y_dtype)) return BL_ERR_INVALID_ARG;
-    if (M == 0 || N == 0) return BL_OK;
-    bl_status st = device_ok();
-    if (st != BL_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M <= bl::kSkinnyMaxM)
-        return launched(
-            bl::launch_forward_skinny(xq, scale, packed, layout, gamma, M, N, K, y, y_dtype, acc, s));
-    return launched(
-        bl::launch_forward_gemm(xq, scale, packed, layout, gamma, M, N, K, y, y_dtype, acc, s));
+    return forward_impl(xq, scale, packed, layout, gamma, bl::GammaMap::single(gamma), M, N, K, y,
+                        y_dtype, acc, stream);
 }
 
 bl_status bitlinear_linear(const void *x, int x_dtype, const uint8_t *packed, int layout,
                            const float *gamma, int64_t M, int64_t N, int64_t K, void *y,
                            int y_dtype, int32_t *acc, void *stream) {
-    if (!x || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(packed) || !aligned16(gamma) || !aligned16(y) ||
-        (acc && !aligned16(acc)))
-        return BL_ERR_INVALID_ARG;
-    if (M < 0 || N < 0 || K < 1 || K > kMaxK || N > 2147483647LL) return BL_ERR_INVALID_ARG;
-    if (!valid_dtype(x_dtype) || !valid_layout(layout) || !valid_dtype(y_dtype))
-        return BL_ERR_INVALID_ARG;
-    if (M > bl::fused_decode_max_m()) return BL_ERR_UNSUPPORTED;
-    if (M == 0 || N == 0) return BL_OK;
-    bl_status st = device_ok();
-    if (st != BL_OK) return st;
-    return launched(bl::launch_linear_decode(x, x_dtype, packed, layout, gamma, M, N, K, y,
-                                             y_dtype, acc, static_cast<hipStream_t>(stream)));
+    return linear_impl(x, x_dtype, packed, layout, gamma, bl::GammaMap::single(gamma), M, N, K, y,
+                       y_dtype, acc, stream);
+}
+
+bl_status bitlinear_forward_segmented(const int8_t *xq, const float *scale, const uint8_t *packed,
+                                      int layout, const float *gammas, const int64_t *seg_rows,
+                                      int nseg, int64_t M, int64_t K, void *y, int y_dtype,
+                                      int32_t *acc, void *stream) {
+    bl::GammaMap gm;
+    int64_t N = 0;
+    if (!make_segments(gammas, seg_rows, nseg, gm, N)) return BL_ERR_INVALID_ARG;
+    return forward_impl(xq, scale, packed, layout, gammas, gm, M, N, K, y, y_dtype, acc, stream);
+}
+
+bl_status bitlinear_linear_segmented(const void *x, int x_dtype, const uint8_t *packed, int layout,
+                                     const float *gammas, const int64_t *seg_rows, int nseg,
+                                     int64_t M, int64_t K, void *y, int y_dtype, int32_t *acc,
+                                     void *stream) {
+    bl::GammaMap gm;
+    int64_t N = 0;
+    if (!make_segments(gammas, seg_rows, nseg, gm, N)) return BL_ERR_INVALID_ARG;
+    return linear_impl(x, x_dtype, packed, layout, gammas, gm, M, N, K, y, y_dtype, acc, stream);
 }
 
 bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,
                                    int layout, const float *gamma, int64_t M, int64_t N,
                                    int64_t K, float *grad_x, void *stream) {
     if (!grad_y || !packed || !gamma || !grad_x) return BL_ERR_INVALID_ARG;
-    if (!aligned16(grad_y) || !aligned16(packed) || !aligned16(gamma) || !aligned16(grad_x))
+    if (!aligned16(grad_y) || !aligned16(packed) || !aligned4(gamma) || !aligned16(grad_x))
         return BL_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return BL_ERR_INVALID_ARG;

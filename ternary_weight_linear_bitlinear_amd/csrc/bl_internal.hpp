@@ -33,6 +33,29 @@ hipError_t allow_dynamic_lds(F *kernel, size_t bytes, int *done) {
     return e;
 }
 
+// Weight scales of a packed matrix whose rows form up to kMaxSegments
+// consecutive segments, each quantised on its own (Q, K and V stacked into one
+// matrix, for instance). Row n belongs to segment s = the number of bounds
+// <= n; a plain matrix is one segment.
+constexpr int kMaxSegments = 8;
+struct GammaMap {
+    const float *g;                     // device array, one gamma per segment
+    int64_t bound[kMaxSegments - 1];    // first row of segments 1 .. nseg - 1
+    int nseg;
+    static GammaMap single(const float *gamma) {
+        GammaMap m{};
+        m.g = gamma;
+        m.nseg = 1;
+        return m;
+    }
+    // the same matrix seen from row `off` on (launches over a column range)
+    GammaMap from_row(int64_t off) const {
+        GammaMap m = *this;
+        for (int i = 0; i < nseg - 1; ++i) m.bound[i] -= off;
+        return m;
+    }
+};
+
 inline int64_t row_bytes_2bit(int64_t K) { return ((K + 3) / 4 + 15) / 16 * 16; }
 inline int64_t row_bytes_base3(int64_t K) { return ((K + 4) / 5 + 15) / 16 * 16; }
 
@@ -50,17 +73,17 @@ hipError_t launch_quant_acts(const void *x, int dtype, int64_t M, int64_t K,
 // ---- products (skinny.hip, gemm.hip) -------------------------------------
 hipError_t launch_forward_skinny(const int8_t *xq, const float *scale,
                                  const uint8_t *packed, int layout,
-                                 const float *gamma, int64_t M, int64_t N,
+                                 const GammaMap &gamma, int64_t M, int64_t N,
                                  int64_t K, void *y, int y_dtype, int32_t *acc,
                                  hipStream_t stream);
 // Fused per-token quantisation + product for M <= fused_decode_max_m().
 int64_t fused_decode_max_m();
 hipError_t launch_linear_decode(const void *x, int x_dtype, const uint8_t *packed, int layout,
-                                const float *gamma, int64_t M, int64_t N, int64_t K, void *y,
+                                const GammaMap &gamma, int64_t M, int64_t N, int64_t K, void *y,
                                 int y_dtype, int32_t *acc, hipStream_t stream);
 hipError_t launch_forward_gemm(const int8_t *xq, const float *scale,
                                const uint8_t *packed, int layout,
-                               const float *gamma, int64_t M, int64_t N,
+                               const GammaMap &gamma, int64_t M, int64_t N,
                                int64_t K, void *y, int y_dtype, int32_t *acc,
                                hipStream_t stream);
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bl_internal.hpp"
+
 namespace bl {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -69,6 +71,36 @@ __device__ __forceinline__ int8_t quant1(float x, float s) {
 // it is not made visible to other waves.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Epilogue factors of a segmented matrix: the gammas are loaded once per
+// workgroup, f_s = gamma_s * scale / 127 (the epilogue's own order of
+// operations) is formed per token, and row n picks its segment's factor.
+__device__ __forceinline__ void load_gammas(const GammaMap &gm, float (&gs)[kMaxSegments]) {
+#pragma unroll
+    for (int s = 0; s < kMaxSegments; ++s) gs[s] = s < gm.nseg ? gm.g[s] : 0.f;
+}
+__device__ __forceinline__ void seg_factors(const GammaMap &gm, const float (&gs)[kMaxSegments],
+                                            float scale, float (&f)[kMaxSegments]) {
+#pragma unroll
+    for (int s = 0; s < kMaxSegments; ++s) f[s] = s < gm.nseg ? gs[s] * scale / 127.0f : 0.f;
+}
+// gamma of row n itself (for epilogues that scale by gamma * (scale / 127))
+__device__ __forceinline__ float seg_gamma(const GammaMap &gm, const float (&gs)[kMaxSegments],
+                                           int64_t n) {
+    float r = gs[0];
+#pragma unroll
+    for (int i = 0; i < kMaxSegments - 1; ++i)
+        if (i < gm.nseg - 1) r = n >= gm.bound[i] ? gs[i + 1] : r;
+    return r;
+}
+__device__ __forceinline__ float seg_pick(const GammaMap &gm, const float (&f)[kMaxSegments],
+                                          int64_t n) {
+    float r = f[0];
+#pragma unroll
+    for (int i = 0; i < kMaxSegments - 1; ++i)
+        r = (i < gm.nseg - 1 && n >= gm.bound[i]) ? f[i + 1] : r;
+    return r;
 }
 
 // Wave-wide (64 lanes) reductions through cross-lane shuffles.

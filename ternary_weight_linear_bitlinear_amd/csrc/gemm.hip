@@ -76,7 +76,7 @@ __device__ __forceinline__ void expand_unit(const uint4 wv, const uint64_t *lut,
 template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, bool EVEN_K, typename YT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ scale,
-    const uint8_t *__restrict__ packed, const float *__restrict__ gamma_p, int64_t M,
+    const uint8_t *__restrict__ packed, const GammaMap gm, int64_t M,
     int64_t N, int64_t K, int64_t rb, int tiles_m, int tiles_n, YT *__restrict__ y, int64_t ldy,
     int32_t *__restrict__ acc_out) {
     using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
@@ -290,12 +290,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     // m = l % 32 (token within fragment i) and n = 8 (r / 4) + 4 (l / 32) +
     // r % 4 (weight row within fragment j): registers 4q..4q+3 are four
     // consecutive outputs of one token, written with one 8- or 16-byte store.
-    const float gamma = gamma_p[0];
+    // One matrix: f = gamma * scale[m] / 127 per token. Stacked segments:
+    // each output scales by its row's gamma times scale[m] / 127.
+    float gs[kMaxSegments];
+    load_gammas(gm, gs);
+    const bool one = gm.nseg == 1;
     const bool full = m0 + BM <= M && n0 + BN <= N && (ldy % 4) == 0;
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) {
         const int64_t m = m0 + wm * (BM / WM) + i * 32 + frow;
-        const float f = gamma * scale[m < M ? m : 0] / 127.0f;
+        const float sm = scale[m < M ? m : 0];
+        const float f1 = gs[0] * sm / 127.0f;
+        const float sm127 = sm / 127.0f;
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
 #pragma unroll
@@ -303,8 +309,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
                 const int64_t n = n0 + wn * (BN / WN) + j * 32 + 8 * q + 4 * lg;
                 const int32_t a0 = acc[i][j][4 * q], a1 = acc[i][j][4 * q + 1];
                 const int32_t a2 = acc[i][j][4 * q + 2], a3 = acc[i][j][4 * q + 3];
-                const float v0 = (float)a0 * f, v1 = (float)a1 * f;
-                const float v2 = (float)a2 * f, v3 = (float)a3 * f;
+                float f[4] = {f1, f1, f1, f1};
+                if (!one) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) f[e] = seg_gamma(gm, gs, n + e) * sm127;
+                }
+                const float v0 = (float)a0 * f[0], v1 = (float)a1 * f[1];
+                const float v2 = (float)a2 * f[2], v3 = (float)a3 * f[3];
                 if (full) {
                     if constexpr (sizeof(YT) == 4) {
                         *reinterpret_cast<float4 *>(y + m * ldy + n) = make_float4(v0, v1, v2, v3);
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 
 template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, typename YT>
 hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t *packed,
-                            const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                            const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                             int64_t ldy, int32_t *acc, hipStream_t s) {
     using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
@@ -363,7 +374,7 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
 // second launch with smaller tiles, so no round runs mostly idle.
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t *packed,
-                            const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                            const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                             int64_t ldy, int32_t *acc, hipStream_t s) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 128) >= 512)
@@ -378,7 +389,7 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
 
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *packed,
-                         const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                         const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                          int32_t *acc, hipStream_t s) {
     constexpr int64_t kCUs = 256;
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
@@ -393,7 +404,8 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
             hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 2, 4, 2>(
                 xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
             if (e != hipSuccess || n_main == N) return e;
-            return launch_gemm_cols<LAYOUT>(xq, scale, packed + n_main * rb, gamma, M, N - n_main,
+            return launch_gemm_cols<LAYOUT>(xq, scale, packed + n_main * rb,
+                                            gamma.from_row(n_main), M, N - n_main,
                                             K, y + n_main, N, acc ? acc + n_main : nullptr, s);
         }
     }
@@ -403,7 +415,7 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
 }  // namespace
 
 hipError_t launch_forward_gemm(const int8_t *xq, const float *scale, const uint8_t *packed,
-                               int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                               int layout, const GammaMap &gamma, int64_t M, int64_t N, int64_t K,
                                void *y, int y_dtype, int32_t *acc, hipStream_t stream) {
     if (M > (int64_t)2147483647 || N > (int64_t)2147483647) return hipErrorInvalidValue;
     if (layout == kLayout2Bit) {

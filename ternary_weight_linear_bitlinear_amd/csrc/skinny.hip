@@ -95,7 +95,7 @@ __device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut,
 template <int LAYOUT, int KS, int NSS, int RG, int MAXM, typename YT>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ scale,
-    const uint8_t *__restrict__ packed, const float *__restrict__ gamma_p, int M, int64_t N,
+    const uint8_t *__restrict__ packed, const GammaMap gm, int M, int64_t N,
     int64_t K, int64_t rb, YT *__restrict__ y, int32_t *__restrict__ acc_out) {
     using C = SkinnyCfg<LAYOUT>;
     constexpr int kThreads = 64 * KS;
@@ -114,7 +114,8 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int r = lane % 16;  // weight row within a row group (A) / token (B)
     const int g = lane / 16;  // lane group = unit within the super-step
     const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
-    const float gamma = gamma_p[0];
+    float gs[kMaxSegments];
+    load_gammas(gm, gs);
 
     if (LAYOUT == kLayoutBase3) {  // visible after the first round's barriers
         for (int i = threadIdx.x; i < 4 * 256; i += kThreads)
@@ -220,7 +221,8 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     for (int q = 0; q < RG; ++q) part[(q * KS + wave) * 64 + lane] = acc[q];
     lds_barrier();
     const int t = r;
-    const float f = t < M ? gamma * scale[t] / 127.0f : 0.f;
+    float fs[kMaxSegments];
+    seg_factors(gm, gs, t < M ? scale[t] : 0.f, fs);
     for (int q = wave; q < RG; q += KS) {  // wave q finishes row group q
         v4i tot = part[(q * KS) * 64 + lane];
 #pragma unroll
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
             const int64_t n = n0 + 16 * q + 4 * g + i;
             if (n >= N) continue;
             const int32_t a = tot[i];
-            const float v = (float)a * f;
+            const float v = (float)a * seg_pick(gm, fs, n);
             if constexpr (sizeof(YT) == 4)
                 y[(int64_t)t * N + n] = v;
             else
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
 
 template <int LAYOUT, int KS, int NSS, int RG, int MAXM, typename YT>
 hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *packed,
-                           const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                           const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int32_t *acc, hipStream_t s) {
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
     // the partial-tile buffer aliases the activation area (needs KS*RG KiB)
@@ -263,7 +265,7 @@ hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *
 
 template <int LAYOUT, typename YT>
 hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *packed,
-                           const float *gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                           const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int32_t *acc, hipStream_t s) {
     // eight waves x two super-steps: one round covers 4096 codes (2-bit) or
     // 5120 (base-3); at M = 16 that is 64 (80) KiB of staged activations
@@ -290,7 +292,7 @@ constexpr int kFusedMaxM = 4;
 template <int LAYOUT, int KS, int NSS, int MAXM, typename XT, typename YT>
 __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const XT *__restrict__ x, const uint8_t *__restrict__ packed,
-    const float *__restrict__ gamma_p, int M, int64_t N, int64_t K, int64_t rb,
+    const GammaMap gm, int M, int64_t N, int64_t K, int64_t rb,
     YT *__restrict__ y, int32_t *__restrict__ acc_out) {
     using C = SkinnyCfg<LAYOUT>;
     constexpr int kThreads = 64 * KS;
@@ -314,7 +316,8 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const uint8_t *wrow = packed + (n0 + r) * rb;
     const bool vec = (K % 8) == 0;
 
-    const float gamma = gamma_p[0];
+    float gs[kMaxSegments];
+    load_gammas(gm, gs);
     uint4 wv[NSS];
     bool wok[NSS];
     auto issue = [&](int64_t u0) {
@@ -496,13 +499,14 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     for (int w = 1; w < KS; ++w) tot += part[w * 64 + lane];
     const int t = r;
     if (t >= M) return;
-    const float f = gamma * tok_scale[t] / 127.0f;
+    float fs[kMaxSegments];
+    seg_factors(gm, gs, tok_scale[t], fs);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t n = n0 + 4 * g + i;
         if (n >= N) continue;
         const int32_t a = tot[i];
-        const float v = (float)a * f;
+        const float v = (float)a * seg_pick(gm, fs, n);
         if constexpr (sizeof(YT) == 4)
             y[(int64_t)t * N + n] = v;
         else
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
 }
 
 template <int LAYOUT, int MAXM, typename XT, typename YT>
-hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const float *gamma, int64_t M,
+hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
     constexpr int KS = kFdKS, NSS = kFdNSS;
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
@@ -531,14 +535,14 @@ hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const float *gamm
 // A one-token specialisation keeps only 16 values of x per thread, which
 // leaves registers for more resident workgroups per CU.
 template <int LAYOUT, typename XT, typename YT>
-hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const float *gamma, int64_t M,
+hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
     if (M == 1) return launch_linear_m<LAYOUT, 1>(x, packed, gamma, M, N, K, y, acc, s);
     return launch_linear_m<LAYOUT, kFusedMaxM>(x, packed, gamma, M, N, K, y, acc, s);
 }
 
 template <int LAYOUT, typename XT>
-hipError_t launch_linear_x(const XT *x, const uint8_t *packed, const float *gamma, int64_t M,
+hipError_t launch_linear_x(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, void *y, int y_dtype, int32_t *acc,
                            hipStream_t s) {
     if (y_dtype == kF32)
@@ -549,7 +553,7 @@ hipError_t launch_linear_x(const XT *x, const uint8_t *packed, const float *gamm
 }  // namespace
 
 hipError_t launch_forward_skinny(const int8_t *xq, const float *scale, const uint8_t *packed,
-                                 int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                                 int layout, const GammaMap &gamma, int64_t M, int64_t N, int64_t K,
                                  void *y, int y_dtype, int32_t *acc, hipStream_t stream) {
     if (layout == kLayout2Bit) {
         if (y_dtype == kF32)
@@ -572,7 +576,7 @@ namespace bl {
 int64_t fused_decode_max_m() { return kFusedMaxM; }
 
 hipError_t launch_linear_decode(const void *x, int x_dtype, const uint8_t *packed, int layout,
-                                const float *gamma, int64_t M, int64_t N, int64_t K, void *y,
+                                const GammaMap &gamma, int64_t M, int64_t N, int64_t K, void *y,
                                 int y_dtype, int32_t *acc, hipStream_t stream) {
     if (layout == kLayout2Bit) {
         if (x_dtype == kF32)

@@ -81,6 +81,7 @@ def _fwd(bl, **kw):
 
 @pytest.mark.parametrize("kw", [
     dict(W=None), dict(packed=None), dict(gamma=None), dict(ws=None), dict(W=P + 4),
+    dict(gamma=P + 2),
     dict(packed=P + 8), dict(N=0), dict(N=-1), dict(K=0), dict(K=16909321), dict(dt=2),
     dict(scheme=5), dict(layout=3), dict(eps=-1.0), dict(eps=float("nan")), dict(wsb=0),
 ])
@@ -98,6 +99,7 @@ def test_quant_rejects(bl, kw):
 
 @pytest.mark.parametrize("kw", [
     dict(xq=None), dict(scale=None), dict(packed=None), dict(gamma=None), dict(y=None),
+    dict(gamma=P + 1),
     dict(y=P + 4), dict(acc=P + 4), dict(M=-1), dict(N=-1), dict(K=0), dict(K=16909321),
     dict(layout=2), dict(ydt=3),
 ])
@@ -142,6 +144,7 @@ def test_backward_rejects_and_limits(bl):
                                                    kw.get("K", 64), kw.get("gx", P), None)
     assert bi(gy=None) == bl.BL_ERR_INVALID_ARG
     assert bi(gamma=None) == bl.BL_ERR_INVALID_ARG
+    assert bi(gamma=P + 2) == bl.BL_ERR_INVALID_ARG
     assert bi(gx=P + 4) == bl.BL_ERR_INVALID_ARG
     assert bi(K=0) == bl.BL_ERR_INVALID_ARG
     assert bi(M=-1) == bl.BL_ERR_INVALID_ARG
@@ -168,3 +171,31 @@ def test_backward_rejects_and_limits(bl):
     if not torch.cuda.is_available():
         assert bi() == bl.BL_ERR_DEVICE
         assert bw() == bl.BL_ERR_DEVICE
+
+
+def test_segmented_rejects(bl):
+    import ctypes
+    lib = bl.library()
+    T = lambda *r: (ctypes.c_int64 * len(r))(*r)
+
+    def fs(table, nseg, **kw):
+        return lib.bitlinear_forward_segmented(P, P, P, kw.get("layout", 0), kw.get("g", P), table,
+                                               nseg, kw.get("M", 4), 64, P, 0, None, None)
+
+    def ls(table, nseg, **kw):
+        return lib.bitlinear_linear_segmented(P, 0, P, 0, kw.get("g", P), table, nseg,
+                                              kw.get("M", 1), 64, P, 0, None, None)
+    for f in (fs, ls):
+        assert f(None, 2) == bl.BL_ERR_INVALID_ARG
+        assert f(T(16, 16), 0) == bl.BL_ERR_INVALID_ARG
+        assert f(T(*([16] * 9)), 9) == bl.BL_ERR_INVALID_ARG
+        assert f(T(16, 0, 16), 3) == bl.BL_ERR_INVALID_ARG
+        assert f(T(16, -4), 2) == bl.BL_ERR_INVALID_ARG
+        assert f(T(16, 16), 2, g=None) == bl.BL_ERR_INVALID_ARG
+        assert f(T(16, 16), 2, g=P + 2) == bl.BL_ERR_INVALID_ARG
+        assert f(T(16, 16), 2, M=0) == bl.BL_OK
+    assert ls(T(16, 16), 2, M=5) == bl.BL_ERR_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        assert fs(T(16, 16), 2) == bl.BL_ERR_DEVICE
+        assert ls(T(*([8] * 8)), 8) == bl.BL_ERR_DEVICE
