@@ -367,8 +367,8 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
     return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, false, YT>, &lds_odd);
 }
 
-// Tile configuration by problem size. Each shape's configuration was chosen
-// by timing on MI355X (see the design notes): large 2-bit problems use
+// Tile configuration by problem size, chosen by timing on MI355X: large
+// 2-bit problems use
 // 256 x 256 tiles with 8 waves; when those tiles do not fill whole rounds of
 // 256 CUs, the columns that do are one launch and the leftover columns a
 // second launch with smaller tiles, so no round runs mostly idle.
@@ -377,7 +377,11 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                             int64_t ldy, int32_t *acc, hipStream_t s) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 128) >= 512)
+    const int64_t t_wide = tiles(256, 128);
+    // 256 x 128 tiles when they make several rounds, or one round that keeps
+    // at least half of the 256 CUs busy (measured faster than two rounds of
+    // 128 x 128 tiles for the leftover columns of the prefill shape)
+    if (t_wide >= 512 || (t_wide >= 128 && t_wide <= 256))
         return launch_gemm_tile<LAYOUT, 256, 128, 2, 4, 2>(xq, scale, packed, gamma, M, N, K, y,
                                                            ldy, acc, s);
     if (tiles(128, 128) >= 256)
