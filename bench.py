@@ -89,8 +89,9 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    def graph_ms(fn, n, warm=1):
-        """Capture fn(0..n-1) into one HIP graph; replay it `warm` times untimed,
+    def graph_ms(fn, n, warm=3):
+        """Capture fn(0..n-1) into one HIP graph; replay it `warm` times untimed
+        (clocks and caches reach steady state),
         then once between two HIP events on the replay stream. Returns ms per call."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -168,12 +169,17 @@ def main():
             r = i % R
             bl.bitlinear_forward(xq_r[r], sc_r[r], copies[r], gamma, p.N, p.K, layout, y=y)
 
+        def gemv_lut(i, copies=copies, gamma=gamma, y=y):
+            r = i % R
+            bl.bitlinear_forward_lut(xq_r[r], sc_r[r], copies[r], gamma, p.N, p.K, y=y)
+
         for i in range(args.warmup):
             step(i)
         # the timed region is one graph replay of exactly `steps` steps
         ms_step = graph_ms(step, args.steps)
         ms_two = graph_ms(step_two, args.steps)
         k_mean = graph_ms(gemv, 2 * R)
+        lut_ms = graph_ms(gemv_lut, 2 * R) if layout == "base3" else None
         # fused kernel: packed weights + bf16 x + gamma + fp32 y
         alg = wbytes + 2 * p.K + 4 + 4 * p.N
         decode[layout] = dict(ms_per_step=ms_step, weight_bytes=wbytes,
@@ -183,8 +189,13 @@ def main():
                               two_launch_ms_per_step=ms_two,
                               forward_only_ms=k_mean,
                               forward_only_gbs=(wbytes + p.K + 8 + 4 * p.N) / (k_mean * 1e-3) / 1e9)
+        if lut_ms is not None:
+            # the same product by activation-side lookup tables (comparison)
+            decode[layout]["lookup_table_forward_ms"] = lut_ms
+            decode[layout]["lookup_table_forward_gbs"] = wbytes / (lut_ms * 1e-3) / 1e9
         log(f"decode {layout}: fused step {ms_step*1e3:.2f} us ({decode[layout]['fused_gbs']:.0f} GB/s), "
-            f"two-launch step {ms_two*1e3:.2f} us, forward only {k_mean*1e3:.2f} us")
+            f"two-launch step {ms_two*1e3:.2f} us, forward only {k_mean*1e3:.2f} us"
+            + (f", lookup-table forward {lut_ms*1e3:.2f} us" if lut_ms is not None else ""))
         del copies
         torch.cuda.empty_cache()
     rows["decode_gemv"] = decode

@@ -172,6 +172,19 @@ bl_status bitlinear_linear_segmented(const void *x, int x_dtype, const uint8_t *
                                      int64_t M, int64_t K, void *y, int y_dtype, int32_t *acc,
                                      void *stream);
 
+/* Alternative decode scheme for the base-3 layout, one token: instead of
+ * expanding each weight byte into five codes, the workgroup tabulates, for
+ * every group of five activations, the partial sums of the first two and the
+ * last three trits (9 + 27 entries) and reads two entries per weight byte
+ * ([b158] §2.3 and §6.3: five weights per byte are unpacked by table lookup
+ * or bit operations). Same arguments and result as bitlinear_forward (acc
+ * bit-identical); kept to compare the lookup scheme with the in-register
+ * decode. Only layout BL_PACK_BASE3 and M = 1 are supported (else
+ * BL_ERR_UNSUPPORTED); M = 0 or N = 0 is a no-op. */
+bl_status bitlinear_forward_lut(const int8_t *xq, const float *scale, const uint8_t *packed,
+                                int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                                void *y, int y_dtype, int32_t *acc, void *stream);
+
 /* Backward products of the straight-through estimator, for training with the
  * codes the forward pass used ([QAT-en] "How Gradients Flow: Fake Quantization
  * and STE": the backward pass treats rounding as the identity, so gradients

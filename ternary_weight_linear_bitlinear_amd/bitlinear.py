@@ -54,6 +54,8 @@ _lib.bitlinear_forward_segmented.argtypes = [_p, _p, _p, _int, _p, _p, _int, _i6
 _lib.bitlinear_linear_segmented.restype = _int
 _lib.bitlinear_linear_segmented.argtypes = [_p, _int, _p, _int, _p, _p, _int, _i64, _i64, _p, _int,
                                             _p, _p]
+_lib.bitlinear_forward_lut.restype = _int
+_lib.bitlinear_forward_lut.argtypes = [_p, _p, _p, _int, _p, _i64, _i64, _i64, _p, _int, _p, _p]
 _lib.bitlinear_backward_input.restype = _int
 _lib.bitlinear_backward_input.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _p]
 _lib.bitlinear_backward_weight.restype = _int
@@ -66,7 +68,7 @@ _lib.bitlinear_version.argtypes = []
 EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
             "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
             "bitlinear_linear", "bitlinear_forward_segmented", "bitlinear_linear_segmented",
-            "bitlinear_backward_input", "bitlinear_backward_weight",
+            "bitlinear_forward_lut", "bitlinear_backward_input", "bitlinear_backward_weight",
             "bitlinear_status_string", "bitlinear_version"]
 FUSED_MAX_M = 4
 
@@ -191,6 +193,24 @@ def bitlinear_linear(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor,
                                  _ptr(gamma), M, N, K, _ptr(y), _DTYPES[y.dtype],
                                  _ptr(acc) if want_acc else None, _stream(stream)),
            "bitlinear_linear")
+    return (y, acc) if want_acc else y
+
+
+def bitlinear_forward_lut(xq: torch.Tensor, scale: torch.Tensor, packed: torch.Tensor,
+                          gamma: torch.Tensor, N: int, K: int, out_dtype=torch.float32,
+                          y: torch.Tensor | None = None, acc: torch.Tensor | bool | None = None,
+                          stream=None):
+    """One token against base-3 codes through activation-side lookup tables."""
+    M = xq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    want_acc = acc is not None and acc is not False
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _check(_lib.bitlinear_forward_lut(_ptr(xq), _ptr(scale), _ptr(packed), BL_PACK_BASE3,
+                                      _ptr(gamma), M, N, K, _ptr(y), _DTYPES[y.dtype],
+                                      _ptr(acc) if want_acc else None, _stream(stream)),
+           "bitlinear_forward_lut")
     return (y, acc) if want_acc else y
 
 

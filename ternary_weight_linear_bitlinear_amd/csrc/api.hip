@@ -193,6 +193,23 @@ bl_status bitlinear_linear_segmented(const void *x, int x_dtype, const uint8_t *
     return linear_impl(x, x_dtype, packed, layout, gammas, gm, M, N, K, y, y_dtype, acc, stream);
 }
 
+bl_status bitlinear_forward_lut(const int8_t *xq, const float *scale, const uint8_t *packed,
+                                int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                                void *y, int y_dtype, int32_t *acc, void *stream) {
+    if (!xq || !scale || !packed || !gamma || !y) return BL_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(scale) || !aligned16(packed) || !aligned4(gamma) ||
+        !aligned16(y) || (acc && !aligned16(acc)))
+        return BL_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || K > kMaxK || N > 2147483647LL) return BL_ERR_INVALID_ARG;
+    if (!valid_layout(layout) || !valid_dtype(y_dtype)) return BL_ERR_INVALID_ARG;
+    if (layout != BL_PACK_BASE3 || M > 1) return BL_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return BL_OK;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    return launched(bl::launch_forward_lut(xq, scale, packed, bl::GammaMap::single(gamma), N, K, y,
+                                           y_dtype, acc, static_cast<hipStream_t>(stream)));
+}
+
 bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,
                                    int layout, const float *gamma, int64_t M, int64_t N,
                                    int64_t K, float *grad_x, void *stream) {

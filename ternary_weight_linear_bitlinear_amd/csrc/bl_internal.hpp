@@ -88,6 +88,11 @@ hipError_t launch_forward_gemm(const int8_t *xq, const float *scale,
                                hipStream_t stream);
 
 
+// One token against base-3 codes by activation-side lookup tables (lut.hip).
+hipError_t launch_forward_lut(const int8_t *xq, const float *scale, const uint8_t *packed,
+                              const GammaMap &gamma, int64_t N, int64_t K, void *y, int y_dtype,
+                              int32_t *acc, hipStream_t stream);
+
 // ---- backward products (backward.hip) ------------------------------------
 // grad_x [M, K] fp32 = gamma * grad_y [M, N] (bf16) x codes of packed [N, rb2(K)].
 hipError_t launch_backward_input(const uint16_t *grad_y, const uint8_t *packed,

@@ -199,3 +199,17 @@ def test_segmented_rejects(bl):
     if not torch.cuda.is_available():
         assert fs(T(16, 16), 2) == bl.BL_ERR_DEVICE
         assert ls(T(*([8] * 8)), 8) == bl.BL_ERR_DEVICE
+
+
+def test_lut_rejects_and_limits(bl):
+    lib = bl.library()
+    f = lambda **kw: lib.bitlinear_forward_lut(kw.get("xq", P), P, P, kw.get("layout", 1), P,
+                                               kw.get("M", 1), kw.get("N", 16), kw.get("K", 64),
+                                               kw.get("y", P), 0, None, None)
+    assert f(xq=None) == bl.BL_ERR_INVALID_ARG
+    assert f(y=P + 4) == bl.BL_ERR_INVALID_ARG
+    assert f(K=0) == bl.BL_ERR_INVALID_ARG
+    assert f(layout=5) == bl.BL_ERR_INVALID_ARG
+    assert f(layout=0) == bl.BL_ERR_UNSUPPORTED
+    assert f(M=2) == bl.BL_ERR_UNSUPPORTED
+    assert f(M=0) == bl.BL_OK and f(N=0) == bl.BL_OK
