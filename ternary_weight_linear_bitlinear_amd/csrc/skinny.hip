@@ -24,11 +24,15 @@ namespace {
 
 // Launch shapes (measured on MI355X with the weights streamed from HBM):
 // eight waves per workgroup, each keeping two 16-byte weight loads per lane
-// in flight, beat four waves with four loads (shorter serial expand/multiply
-// chain per wave once the data lands). Batches at N >= 8192 put two row
-// groups in a workgroup, halving the activation staging per weight byte.
+// in flight, beat four waves with four loads when there are few workgroups
+// per CU (shorter serial expand/multiply chain per wave once the data lands;
+// long rows). From kWideN rows on (at least four workgroups per CU) four waves
+// with four loads keep more bytes in flight per CU and stream faster.
+// Batches at N >= 8192 put two row groups in a workgroup, halving the
+// activation staging per weight byte.
 constexpr int kSkKS = 8, kSkNSS = 2, kSkRG2MinN = 8192;
 constexpr int kFdKS = 8, kFdNSS = 2;
+constexpr int64_t kWideN = 16384;
 
 // 16 elements of x held as raw 16-byte pieces (two for bf16, four for fp32),
 // widened to fp32.
@@ -269,6 +273,9 @@ hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *
                            int32_t *acc, hipStream_t s) {
     // eight waves x two super-steps: one round covers 4096 codes (2-bit) or
     // 5120 (base-3); at M = 16 that is 64 (80) KiB of staged activations
+    if (M <= 4 && N >= kWideN)
+        return launch_skinny_t<LAYOUT, 4, 4, 1, 4, YT>(xq, scale, packed, gamma, M, N, K, y, acc,
+                                                      s);
     if (M <= 4)
         return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 1, 4, YT>(xq, scale, packed, gamma, M, N, K,
                                                                y, acc, s);
@@ -515,10 +522,9 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     }
 }
 
-template <int LAYOUT, int MAXM, typename XT, typename YT>
+template <int LAYOUT, int MAXM, int KS, int NSS, typename XT, typename YT>
 hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
-    constexpr int KS = kFdKS, NSS = kFdNSS;
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
     const size_t act = (size_t)MAXM * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) +
@@ -537,8 +543,13 @@ hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &g
 template <int LAYOUT, typename XT, typename YT>
 hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
-    if (M == 1) return launch_linear_m<LAYOUT, 1>(x, packed, gamma, M, N, K, y, acc, s);
-    return launch_linear_m<LAYOUT, kFusedMaxM>(x, packed, gamma, M, N, K, y, acc, s);
+    if (N >= kWideN) {
+        if (M == 1) return launch_linear_m<LAYOUT, 1, 4, 4>(x, packed, gamma, M, N, K, y, acc, s);
+        return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4>(x, packed, gamma, M, N, K, y, acc, s);
+    }
+    if (M == 1)
+        return launch_linear_m<LAYOUT, 1, kFdKS, kFdNSS>(x, packed, gamma, M, N, K, y, acc, s);
+    return launch_linear_m<LAYOUT, kFusedMaxM, kFdKS, kFdNSS>(x, packed, gamma, M, N, K, y, acc, s);
 }
 
 template <int LAYOUT, typename XT>

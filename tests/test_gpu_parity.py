@@ -109,6 +109,8 @@ FWD_CASES = [
     (257, 257, 320), (33, 1, 160), (128, 128, 4096), (300, 512, 129),
     # enough 256 x 256 tiles for a full round plus leftover columns
     (4096, 4357, 64), (2048, 8200, 48),
+    # many rows at M <= 4 (the four-wave weight-streaming launch shape)
+    (2, 16400, 96), (1, 16384, 33),
 ]
 
 
@@ -243,7 +245,8 @@ def test_zero_activation_row_gives_zero_output(bl):
 @pytest.mark.parametrize("layout", ["2bit", "base3"])
 @pytest.mark.parametrize("M,N,K,dtype", [(1, 256, 256, "f32"), (2, 100, 1000, "bf16"),
                                          (3, 33, 17, "f32"), (4, 300, 4099, "bf16"),
-                                         (1, 4096, 11008, "bf16"), (4, 64, 8192, "f32")])
+                                         (1, 4096, 11008, "bf16"), (4, 64, 8192, "f32"),
+                                         (1, 16400, 160, "bf16"), (3, 16384, 5000, "f32")])
 def test_fused_linear_parity(bl, layout, M, N, K, dtype):
     """Same activation codes as the stand-alone quantiser (bit-exact), hence
     the same INT32 accumulators as the oracle, and y within tolerance."""
