@@ -376,8 +376,9 @@ def main():
 
     # ------------------------------------------------- bf16 comparison lines
     # What a GPU without ternary kernels runs: the same layers with dense bf16
-    # weights through the vendor GEMM (torch linear -> hipBLASLt). Context for
-    # the ternary path's numbers, not part of the path.
+    # weights through the vendor GEMM (torch linear -> hipBLASLt), and the vendor
+    # dense INT8 GEMM on the prefill shape. Context for the ternary path's
+    # numbers, not part of the path.
     if want("bf16_baseline"):
         log("bf16 dense baseline (torch linear)")
         base = {}
@@ -404,8 +405,15 @@ def main():
         if "prefill_gemm" in rows:
             base["prefill_gemm_bf16"]["ternary_speedup"] = ms / rows["prefill_gemm"]["2bit"]["gemm_ms"]
         log(f"bf16 prefill GEMM: {ms*1e3:.1f} us ({base['prefill_gemm_bf16']['tflops']:.0f} TFLOP/s)")
+        # dense INT8 x INT8 -> INT32 on the same shape (torch._int_mm -> hipBLASLt)
+        xi = torch.randint(-127, 128, (q["M"], q["K"]), dtype=torch.int8, device=dev)
+        wi = torch.randint(-1, 2, (q["K"], q["N"]), dtype=torch.int8, device=dev)
+        ms = graph_ms(lambda i: torch._int_mm(xi, wi), 10)
+        base["prefill_gemm_int8_dense"] = dict(ms=ms, tops=ops / (ms * 1e-3) / 1e12,
+                                               frac=ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS)
+        log(f"dense int8 prefill GEMM: {ms*1e3:.1f} us ({base['prefill_gemm_int8_dense']['tops']:.0f} TOPS)")
         rows["bf16_dense_baseline"] = base
-        del xb, Wb
+        del xb, Wb, xi, wi
         torch.cuda.empty_cache()
 
     # --------------------------------------------------------- CPU baseline
