@@ -89,10 +89,11 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    def graph_ms(fn, n, warm=3):
-        """Capture fn(0..n-1) into one HIP graph; replay it `warm` times untimed
-        (clocks and caches reach steady state),
-        then once between two HIP events on the replay stream. Returns ms per call."""
+    def graph_ms(fn, n, warm=3, warm_ms=25.0):
+        """Capture fn(0..n-1) into one HIP graph; replay it untimed at least `warm`
+        times and for at least `warm_ms` of GPU time (clocks and caches reach steady
+        state: heavy GEMMs run ~10% slower in the first tens of milliseconds), then
+        once between two HIP events on the replay stream. Returns ms per call."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -103,9 +104,16 @@ def main():
         with torch.cuda.graph(g):
             for i in range(n):
                 fn(i)
-        for _ in range(warm):
-            g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spent, reps = 0.0, 0
+        while reps < warm or spent < warm_ms:
+            torch.cuda.synchronize()
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            spent += a.elapsed_time(b)
+            reps += 1
         torch.cuda.synchronize()
         a.record()
         g.replay()
