@@ -73,24 +73,46 @@ __device__ __forceinline__ void expand_unit(const uint4 wv, const uint64_t *lut,
     }
 }
 
+// One product over a column range of the packed matrix: y[:, 0:N] (row stride
+// ldy) from packed rows 0..N-1.
+template <typename YT>
+struct GemmArgs {
+    const int8_t *xq;
+    const float *scale;
+    const uint8_t *packed;
+    GammaMap gm;
+    int64_t M, N, K, rb;
+    int tiles_m, tiles_n;
+    YT *y;
+    int64_t ldy;
+    int32_t *acc_out;
+};
+
+// Block b of nblocks -> tile index: each of the eight XCDs (dispatched
+// round-robin by block id) gets a contiguous run of tiles, which share
+// activation rows in its L2. -1 past the last tile.
+__device__ __forceinline__ int xcd_tile(int b, int ntiles) {
+    const int per_xcd = (ntiles + kXcds - 1) / kXcds;
+    const int t = (b % kXcds) * per_xcd + b / kXcds;
+    return t < ntiles ? t : -1;
+}
+
 template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, bool EVEN_K, typename YT>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
-    const int8_t *__restrict__ xq, const float *__restrict__ scale,
-    const uint8_t *__restrict__ packed, const GammaMap gm, int64_t M,
-    int64_t N, int64_t K, int64_t rb, int tiles_m, int tiles_n, YT *__restrict__ y, int64_t ldy,
-    int32_t *__restrict__ acc_out) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
     constexpr int kThreads = C::kThreads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem);
     int8_t *stage0 = reinterpret_cast<int8_t *>(smem + C::LUT);
+    const int8_t *__restrict__ xq = g.xq;
+    const float *__restrict__ scale = g.scale;
+    const uint8_t *__restrict__ packed = g.packed;
+    const GammaMap &gm = g.gm;
+    const int64_t M = g.M, N = g.N, K = g.K, rb = g.rb, ldy = g.ldy;
+    const int tiles_n = g.tiles_n;
+    YT *__restrict__ y = g.y;
+    int32_t *__restrict__ acc_out = g.acc_out;
 
-    // XCD-aware tile mapping
-    const int ntiles = tiles_m * tiles_n;
-    const int per_xcd = (ntiles + kXcds - 1) / kXcds;
-    const int b = blockIdx.x;
-    const int t = (b % kXcds) * per_xcd + b / kXcds;
-    if (t >= ntiles) return;
     const int64_t m0 = (int64_t)(t / tiles_n) * BM;
     const int64_t n0 = (int64_t)(t % tiles_n) * BN;
 
@@ -346,6 +368,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     }
 }
 
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, bool EVEN_K, typename YT>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs<YT> g) {
+    const int t = xcd_tile(blockIdx.x, g.tiles_m * g.tiles_n);
+    if (t < 0) return;
+    gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, EVEN_K, YT>(g, t);
+}
+
+// The prefill shape in one launch: the first blocks cover the columns that
+// fill whole rounds of 256 x 256 tiles, the rest the leftover columns in
+// 256 x 128 tiles. Leftover tiles start as soon as CUs free up, so their
+// start-up overlaps the output writes of the large tiles (and no second
+// launch is waited for).
+template <int LAYOUT, bool EVEN_K, typename YT>
+__global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, int blocks1,
+                                                        const GemmArgs<YT> g2) {
+    const int b = blockIdx.x;
+    if (b < blocks1) {
+        const int t = xcd_tile(b, g1.tiles_m * g1.tiles_n);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 2, 4, 2, EVEN_K, YT>(g1, t);
+    } else {
+        const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, EVEN_K, YT>(g2, t);
+    }
+}
+
 template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, typename YT>
 hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
@@ -355,11 +402,11 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const int64_t ntiles = (int64_t)tm * tn;
     const int64_t blocks = (ntiles + kXcds - 1) / kXcds * kXcds;
+    const GemmArgs<YT> g{xq, scale, packed, gamma, M, N, K, rb, tm, tn, y, ldy, acc};
     auto launch = [&](auto kern, int *flag) {
         hipError_t e = allow_dynamic_lds(kern, C::SMEM, flag);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::SMEM, s, xq, scale,
-                           packed, gamma, M, N, K, rb, tm, tn, y, ldy, acc);
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::SMEM, s, g);
         return hipGetLastError();
     };
     static int lds_even = 0, lds_odd = 0;
@@ -391,6 +438,35 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
                                                       acc, s);
 }
 
+// Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in 256 x 128 tiles,
+// one launch (2-bit).
+template <int LAYOUT, typename YT>
+hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t *packed,
+                            const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t n_main,
+                            YT *y, int32_t *acc, hipStream_t s) {
+    using C1 = GemmCfg<LAYOUT, 256, 256, 2, 4, 2>;
+    using C2 = GemmCfg<LAYOUT, 256, 128, 2, 4, 2>;
+    static_assert(C1::SMEM == C2::SMEM && C1::kThreads == C2::kThreads, "one launch shape");
+    const int64_t rb = row_bytes_2bit(K);
+    const int tm = (int)((M + 255) / 256);
+    const int tn1 = (int)((n_main + 255) / 256), tn2 = (int)((N - n_main + 127) / 128);
+    const GemmArgs<YT> g1{xq, scale, packed, gamma, M, n_main, K, rb, tm, tn1, y, N, acc};
+    const GemmArgs<YT> g2{xq, scale, packed + n_main * rb, gamma.from_row(n_main), M, N - n_main,
+                          K, rb, tm, tn2, y + n_main, N, acc ? acc + n_main : nullptr};
+    const int blocks1 = (tm * tn1 + kXcds - 1) / kXcds * kXcds;
+    const int blocks2 = (tm * tn2 + kXcds - 1) / kXcds * kXcds;
+    auto launch = [&](auto kern, int *flag) {
+        hipError_t e = allow_dynamic_lds(kern, C1::SMEM, flag);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(blocks1 + blocks2)), dim3(C1::kThreads), C1::SMEM,
+                           s, g1, blocks1, g2);
+        return hipGetLastError();
+    };
+    static int lds_even = 0, lds_odd = 0;
+    if (K % 16 == 0) return launch(gemm_pair_kernel<LAYOUT, true, YT>, &lds_even);
+    return launch(gemm_pair_kernel<LAYOUT, false, YT>, &lds_odd);
+}
+
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *packed,
                          const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
@@ -405,6 +481,11 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
             int64_t tn_main = rounds * kCUs / tm;
             if (tn_main > tn) tn_main = tn;
             const int64_t n_main = tn_main * 256 < N ? tn_main * 256 : N;
+            const int64_t n_rest = N - n_main;
+            const int64_t t_rest = tm * ((n_rest + 127) / 128);
+            if (n_rest > 0 && t_rest >= 128 && t_rest <= kCUs)
+                return launch_gemm_pair<LAYOUT>(xq, scale, packed, gamma, M, N, K, n_main, y, acc,
+                                                s);
             hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 2, 4, 2>(
                 xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
             if (e != hipSuccess || n_main == N) return e;
