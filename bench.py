@@ -61,7 +61,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is described, not run.", file=sys.stderr)
         sys.exit(2)
 

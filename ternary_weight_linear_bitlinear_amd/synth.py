@@ -81,8 +81,9 @@ def make_problem(M: int, N: int, K: int, seed: int, dtype: str = "f32",
     return Problem(name, M, N, K, dtype, w, x, w, x, g, g)
 
 
-# Workloads. Sizes, dtypes and distributions follow the five configurations of
-# the method's measurement plan; seeds are fixed per configuration.
+# Workloads: a tiny single layer, the decode GEMV, the prefill GEMM, one
+# transformer block's six linear layers and the training step, with LLM-like
+# shapes (hidden 4096, FFN 11008); seeds are fixed per workload.
 WORKLOADS = {
     # single BitLinear forward, fp32 in and out, 2-bit packing
     "tiny": dict(M=8, N=256, K=256, seed=1, dtype="f32"),
