@@ -219,7 +219,8 @@ __global__ __launch_bounds__(kThreads) void pack_base3_kernel(
 // 8-element chunks t, t + 256, ..., kept in registers between the max
 // reduction and the quantisation (J chunks per thread; J = 0 re-reads the
 // row from cache for rows longer than 8 * 256 * 8 elements). Each code is
-// quant1() (device_util.hpp): division, then * 127, then round half to even.
+// quant1() (device_util.hpp): x / s (correctly rounded), then * 127, then round
+// half to even.
 __device__ __forceinline__ float block_max(float v) {
     __shared__ float red[kThreads / 64];
     v = wave_max(v);
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(kThreads) void quant_acts_kernel(
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
         }
         const float s = fmaxf(block_max(amax), 1e-6f);
+        const float y = 1.0f / s;
         if (threadIdx.x == 0) scale[m] = s;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -272,22 +274,23 @@ __global__ __launch_bounds__(kThreads) void quant_acts_kernel(
                 uint32_t lo = 0, hi = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    lo |= (uint32_t)(uint8_t)quant1(v[j][e], s) << (8 * e);
-                    hi |= (uint32_t)(uint8_t)quant1(v[j][e + 4], s) << (8 * e);
+                    lo |= (uint32_t)(uint8_t)quant1(v[j][e], s, y) << (8 * e);
+                    hi |= (uint32_t)(uint8_t)quant1(v[j][e + 4], s, y) << (8 * e);
                 }
                 *reinterpret_cast<uint2 *>(out + c * 8) = make_uint2(lo, hi);
             } else {
                 for (int e = 0; e < 8; ++e)
-                    if (c * 8 + e < K) out[c * 8 + e] = quant1(v[j][e], s);
+                    if (c * 8 + e < K) out[c * 8 + e] = quant1(v[j][e], s, y);
             }
         }
     } else {
         for (int64_t k = threadIdx.x; k < K; k += kThreads)
             amax = fmaxf(amax, fabsf(Elem<T>::get(row, k)));
         const float s = fmaxf(block_max(amax), 1e-6f);
+        const float y = 1.0f / s;
         if (threadIdx.x == 0) scale[m] = s;
         for (int64_t k = threadIdx.x; k < K; k += kThreads)
-            out[k] = quant1(Elem<T>::get(row, k), s);
+            out[k] = quant1(Elem<T>::get(row, k), s, y);
     }
 }
 

@@ -449,10 +449,11 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
 
     auto store_codes = [&](int t, int cc, const float *v) {
         const float sc = tok_scale[t];
+        const float rc = 1.0f / sc;
         uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            d[e / 4] |= (uint32_t)(uint8_t)quant1(v[e], sc) << (8 * (e % 4));
+            d[e / 4] |= (uint32_t)(uint8_t)quant1(v[e], sc, rc) << (8 * (e % 4));
         *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) =
             v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
     };

@@ -102,6 +102,51 @@ def test_quant_acts_parity(bl, M, K, dtype, outl):
     assert n_ex == 0, "same fp32 steps on both sides: no boundary mismatch expected"
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_quant_acts_half_integer_boundaries(bl, fused):
+    """Activations placed on and one ulp around x = s (k + 1/2) / 127 for every
+    k, where the code is decided by the last bit of the fp32 quotient and the
+    round-half-to-even rule: every code must equal the oracle's (IEEE division
+    in the pages' order), boundary elements included."""
+    banner(f"quant half-integer boundaries fused={fused}")
+    rng = np.random.default_rng(4242)
+    rows = []
+    for s in (np.float32(127.0), np.float32(1.0), np.float32(3.7), np.float32(20.0),
+              np.float32(0.0123), np.float32(1e-3)):
+        k = np.arange(-127, 127, dtype=np.float64)
+        base = (s.astype(np.float64) * (k + 0.5) / 127.0).astype(np.float32)
+        vals = np.concatenate([base, np.nextafter(base, np.float32(np.inf)),
+                               np.nextafter(base, np.float32(-np.inf))])
+        vals = vals[np.abs(vals) <= s]
+        row = np.zeros(1024, np.float32)
+        row[:vals.size] = rng.permutation(vals)
+        row[vals.size] = s  # the row maximum fixes the scale
+        rows.append(row)
+    x = np.stack(rows).astype(np.float32)
+    xq_ref, s_ref, flags = oracle.quant_acts(x)
+    assert flags.any()  # the case does exercise rounding boundaries
+    if not fused:
+        xq, scale = bl.bitlinear_quant_acts(dev(x))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(scale), s_ref)
+        assert np.array_equal(to_np(xq), xq_ref), "codes differ at a rounding boundary"
+    else:
+        # the fused decode step quantises inside the product: compare through
+        # the accumulators against single-code weight rows (acc = one code)
+        K = x.shape[1]
+        for t in range(0, x.shape[0], 4):
+            xs = np.ascontiguousarray(x[t:t + 4])
+            M = xs.shape[0]
+            codes = np.zeros((K, K), np.int8)
+            np.fill_diagonal(codes, 1)
+            packed = oracle.pack(codes, "2bit")
+            g = torch.tensor([1.0, 0, 0, 0], dtype=torch.float32, device="cuda")
+            y, acc = bl.bitlinear_linear(dev(xs), dev(packed), g, K, "2bit", acc=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(acc), xq_ref[t:t + M].astype(np.int32)), \
+                "fused codes differ at a rounding boundary"
+
+
 # ----------------------------------------------------------------------------
 FWD_CASES = [
     (1, 256, 256), (1, 31, 100), (2, 300, 1000), (3, 64, 64), (5, 16, 1), (8, 256, 256),
