@@ -60,14 +60,32 @@ __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
 // residual r underflows, which needs |x / s| < 2^-80; such a quotient rounds
 // to code 0 either way. (An exhaustive run over every bf16 x against 20000
 // scales found differing quotients only below 2^-88, never a differing code.)
-__device__ __forceinline__ int8_t quant1(float x, float s, float y) {
+//
+// Rounding and the clamp cost no instructions of their own. s is the largest
+// |x| of the token (or 1e-6 above it), so for finite x the quotient lies
+// within one ulp of [-1, 1] and t = q * 127 within [-127.0001, 127.0001]: the
+// clamp can never change the rounded value. Adding 1.5 * 2^23 rounds t to an
+// integer (half to even, the default rounding of the add) and leaves that
+// integer in the low mantissa bits, so the low byte of the sum's bit pattern
+// is the two's-complement code. The multiply and the add stay two rounded
+// operations (the library is built without floating-point contraction).
+__device__ __forceinline__ uint32_t quant_word(float x, float s, float y) {
     const float q0 = x * y;
     const float r = __builtin_fmaf(-q0, s, x);
-    float t = __builtin_fmaf(r, y, q0);
-    t = t * 127.0f;
-    float q = rintf(t);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int8_t)(int)q;
+    const float t = __builtin_fmaf(r, y, q0) * 127.0f;
+    return __float_as_uint(t + 12582912.0f);
+}
+__device__ __forceinline__ int8_t quant1(float x, float s, float y) {
+    return (int8_t)(quant_word(x, s, y) & 0xFFu);
+}
+// Four codes packed little-endian into one word (three byte permutes).
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, float s,
+                                           float y) {
+    const uint32_t lo = __builtin_amdgcn_perm(quant_word(x1, s, y), quant_word(x0, s, y),
+                                              0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(quant_word(x3, s, y), quant_word(x2, s, y),
+                                              0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void pack_base3_kernel(
 // 8-element chunks t, t + 256, ..., kept in registers between the max
 // reduction and the quantisation (J chunks per thread; J = 0 re-reads the
 // row from cache for rows longer than 8 * 256 * 8 elements). Each code is
-// quant1() (device_util.hpp): x / s (correctly rounded), then * 127, then round
+// quant_word() (device_util.hpp): x / s (correctly rounded), then * 127, then round
 // half to even.
 __device__ __forceinline__ float block_max(float v) {
     __shared__ float red[kThreads / 64];
@@ -271,13 +271,10 @@ __global__ __launch_bounds__(kThreads) void quant_acts_kernel(
             const int64_t c = threadIdx.x + (int64_t)j * kThreads;
             if (c >= nchunk) continue;
             if (vec) {
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lo |= (uint32_t)(uint8_t)quant1(v[j][e], s, y) << (8 * e);
-                    hi |= (uint32_t)(uint8_t)quant1(v[j][e + 4], s, y) << (8 * e);
-                }
-                *reinterpret_cast<uint2 *>(out + c * 8) = make_uint2(lo, hi);
+                const float *w = v[j];
+                *reinterpret_cast<uint2 *>(out + c * 8) =
+                    make_uint2(quant4(w[0], w[1], w[2], w[3], s, y),
+                               quant4(w[4], w[5], w[6], w[7], s, y));
             } else {
                 for (int e = 0; e < 8; ++e)
                     if (c * 8 + e < K) out[c * 8 + e] = quant1(v[j][e], s, y);

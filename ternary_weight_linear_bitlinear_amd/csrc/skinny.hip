@@ -291,7 +291,7 @@ hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *
 // inside every block, then the same weight-streaming product. Each block
 // loads its chunks of x (from L2), issues its weight loads, derives the token
 // scales s_m = max(max|x|, 1e-6) and quantises the round's slice of x into
-// LDS with quant1() (the same fp32 steps as the stand-alone quantiser, so
+// LDS with quant4() (the same fp32 steps as the stand-alone quantiser, so
 // codes are identical) while the weights are still in flight, then
 // multiplies. One launch instead of two on the latency-bound decode path.
 constexpr int kFusedMaxM = 4;
@@ -450,12 +450,11 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     auto store_codes = [&](int t, int cc, const float *v) {
         const float sc = tok_scale[t];
         const float rc = 1.0f / sc;
-        uint32_t d[4] = {0u, 0u, 0u, 0u};
+        v4i d;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            d[e / 4] |= (uint32_t)(uint8_t)quant1(v[e], sc, rc) << (8 * (e % 4));
-        *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) =
-            v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+        for (int i = 0; i < 4; ++i)
+            d[i] = (int)quant4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], sc, rc);
+        *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) = d;
     };
 
     v4i acc = {0, 0, 0, 0};
