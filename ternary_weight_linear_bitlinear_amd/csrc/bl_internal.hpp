@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -31,6 +32,21 @@ hipError_t allow_dynamic_lds(F *kernel, size_t bytes, int *done) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e == hipSuccess) *done = 1;
     return e;
+}
+
+// Compute units of the current device, queried once per device; 0 if the
+// query fails (callers then size grids without it).
+inline int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0 &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Weight scales of a packed matrix whose rows form up to kMaxSegments

@@ -295,8 +295,14 @@ hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *
 // codes are identical) while the weights are still in flight, then
 // multiplies. One launch instead of two on the latency-bound decode path.
 constexpr int kFusedMaxM = 4;
+// Streaming variant (several tokens, many tiles): grid capped at two blocks per
+// compute unit, 8 waves of 2 units each, one tile of weights in flight ahead
+// (one, three or four blocks per unit, 4-wave blocks and two tiles ahead were
+// all slower on MI355X at N = 6144 .. 22016).
+constexpr int kFusedBlocksPerCu = 2;
+constexpr int kFsKS = 8, kFsNSS = 2;
 
-template <int LAYOUT, int KS, int NSS, int MAXM, typename XT, typename YT>
+template <int LAYOUT, int KS, int NSS, int MAXM, bool STREAM, typename XT, typename YT>
 __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const XT *__restrict__ x, const uint8_t *__restrict__ packed,
     const GammaMap gm, int M, int64_t N, int64_t K, int64_t rb,
@@ -306,10 +312,14 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     constexpr int kRoundUnits = KS * NSS * 4;
     constexpr int kRoundK = kRoundUnits * C::kUnitCodes;
     constexpr int kActStride = kRoundK + 16;
+    // STREAM: the block streams tiles (see below); otherwise it owns one tile
+    // and keeps the register count that lets more blocks stay resident.
+    constexpr bool kStream = STREAM;
+    // LDS: [base-3 table] [activation tile, MAXM rows] [two partial-sum areas]
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem);
     int8_t *act = reinterpret_cast<int8_t *>(smem + (LAYOUT == kLayoutBase3 ? 8192 : 0));
-    v4i *part = reinterpret_cast<v4i *>(act);
+    v4i *part = reinterpret_cast<v4i *>(act + MAXM * kActStride);
     __shared__ float red[kFusedMaxM][KS];
     __shared__ float tok_scale[kFusedMaxM];
 
@@ -317,24 +327,25 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const int lane = threadIdx.x % 64;
     const int r = lane % 16;
     const int g = lane / 16;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t tiles = (N + 15) / 16;  // 16 weight rows per tile
     const int64_t units = rb / 16;
-    const bool row_ok = n0 + r < N;
-    const uint8_t *wrow = packed + (n0 + r) * rb;
     const bool vec = (K % 8) == 0;
 
     float gs[kMaxSegments];
     load_gammas(gm, gs);
-    uint4 wv[NSS];
-    bool wok[NSS];
-    auto issue = [&](int64_t u0) {
+    // this lane's weight units of tile `tile`, round starting at unit u0
+    uint4 wv[NSS], wn[NSS];
+    bool wok[NSS], wnok[NSS];
+    auto issue = [&](int64_t tile, int64_t u0, uint4 (&w)[NSS], bool (&ok)[NSS]) {
+        const int64_t n = tile * 16 + r;
+        const uint8_t *wrow = packed + n * rb;
 #pragma unroll
         for (int s = 0; s < NSS; ++s) {
             const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
-            wok[s] = row_ok && unit < units;
+            ok[s] = n < N && unit < units;
             // out-of-range lanes read a valid address; the value is zeroed
             // where it is consumed, so no wait is forced here
-            wv[s] = *reinterpret_cast<const uint4 *>(wok[s] ? wrow + unit * 16 : packed);
+            w[s] = *reinterpret_cast<const uint4 *>(ok[s] ? wrow + unit * 16 : packed);
         }
     };
 
@@ -367,7 +378,12 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
             for (int j = 0; j < kRaw; ++j) xr[i][j] = src[j];
         }
     }
-    issue(0);
+    const int64_t tile0 = blockIdx.x;
+    issue(tile0, 0, wv, wok);
+    // streaming (rows that fit one round): x is quantised once per block and
+    // the block takes tiles tile0, tile0 + gridDim.x, ...; the next tile's
+    // weights are always in flight while the current one is multiplied
+    if (kStream && one_round && tile0 + gridDim.x < tiles) issue(tile0 + gridDim.x, 0, wn, wnok);
 
     if (LAYOUT == kLayoutBase3) {
         for (int i = threadIdx.x; i < 4 * 256; i += kThreads)
@@ -457,99 +473,140 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) = d;
     };
 
-    v4i acc = {0, 0, 0, 0};
-    for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
-        if (u0 > 0) {
-            issue(u0);
-            lds_barrier();  // previous round's readers are done
-        }
-        // quantise x[0:M, k0 : k0 + kRoundK] into LDS (zero past K)
-        const int64_t k0 = u0 * C::kUnitCodes;
-        if (one_round) {
+    if (one_round) {
 #pragma unroll
-            for (int i = 0; i < kMaxQ; ++i) {
-                const int q = threadIdx.x + i * kThreads;
-                if (q < M * kChunksPerTok) store_codes(q / kChunksPerTok, q % kChunksPerTok, xv[i]);
-            }
-        } else {
-            for (int q = threadIdx.x; q < M * kChunksPerTok; q += kThreads) {
-                const int t = q / kChunksPerTok, cc = q % kChunksPerTok;
-                float v[16];
-                load_chunk(t, k0 + cc * 16, v);
-                store_codes(t, cc, v);
-            }
+        for (int i = 0; i < kMaxQ; ++i) {
+            const int q = threadIdx.x + i * kThreads;
+            if (q < M * kChunksPerTok) store_codes(q / kChunksPerTok, q % kChunksPerTok, xv[i]);
         }
         lds_barrier();
-#pragma unroll
-        for (int s = 0; s < NSS; ++s) {
-            int c[20];
-            decode_unit<LAYOUT>(wok[s] ? wv[s] : make_uint4(0u, 0u, 0u, 0u), lut, c);
-            const int ul = (s * KS + wave) * 4 + g;
-#pragma unroll
-            for (int st = 0; st < C::kSteps; ++st) {
-                v4i b = {0, 0, 0, 0};
-                if (r < M)
-                    b = *reinterpret_cast<const v4i *>(act + r * kActStride +
-                                                       ul * C::kUnitCodes + 16 * st);
-                const v4i a = {c[4 * st], c[4 * st + 1], c[4 * st + 2], c[4 * st + 3]};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
-            }
-        }
     }
 
-    lds_barrier();
-    part[wave * 64 + lane] = acc;
-    lds_barrier();
-    if (wave != 0) return;
-    v4i tot = part[lane];
+    int buf = 0;
+    for (int64_t tile = tile0; tile < tiles; tile += gridDim.x) {
+        v4i acc = {0, 0, 0, 0};
+        for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
+            if (!one_round) {
+                if (u0 > 0 || tile != tile0) {
+                    issue(tile, u0, wv, wok);
+                    lds_barrier();  // previous round's readers are done
+                }
+                // quantise x[0:M, k0 : k0 + kRoundK] into LDS (zero past K)
+                const int64_t k0 = u0 * C::kUnitCodes;
+                for (int q = threadIdx.x; q < M * kChunksPerTok; q += kThreads) {
+                    const int t = q / kChunksPerTok, cc = q % kChunksPerTok;
+                    float v[16];
+                    load_chunk(t, k0 + cc * 16, v);
+                    store_codes(t, cc, v);
+                }
+                lds_barrier();
+            }
 #pragma unroll
-    for (int w = 1; w < KS; ++w) tot += part[w * 64 + lane];
-    const int t = r;
-    if (t >= M) return;
-    float fs[kMaxSegments];
-    seg_factors(gm, gs, tok_scale[t], fs);
+            for (int s = 0; s < NSS; ++s) {
+                int c[20];
+                decode_unit<LAYOUT>(wok[s] ? wv[s] : make_uint4(0u, 0u, 0u, 0u), lut, c);
+                const int ul = (s * KS + wave) * 4 + g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t n = n0 + 4 * g + i;
-        if (n >= N) continue;
-        const int32_t a = tot[i];
-        const float v = (float)a * seg_pick(gm, fs, n);
-        if constexpr (sizeof(YT) == 4)
-            y[(int64_t)t * N + n] = v;
-        else
-            y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
-        if (acc_out) acc_out[(int64_t)t * N + n] = a;
+                for (int st = 0; st < C::kSteps; ++st) {
+                    v4i b = {0, 0, 0, 0};
+                    if (r < M)
+                        b = *reinterpret_cast<const v4i *>(act + r * kActStride +
+                                                           ul * C::kUnitCodes + 16 * st);
+                    const v4i a = {c[4 * st], c[4 * st + 1], c[4 * st + 2], c[4 * st + 3]};
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+                }
+            }
+        }
+        if (kStream && one_round) {
+            const int64_t ahead = tile + 2 * (int64_t)gridDim.x;
+#pragma unroll
+            for (int s = 0; s < NSS; ++s) {
+                wv[s] = wn[s];
+                wok[s] = wnok[s];
+            }
+            if (ahead < tiles) issue(ahead, 0, wn, wnok);
+        }
+
+        // sum over the waves through LDS; two areas, so one barrier per tile
+        // suffices (an area is rewritten only after the next tile's barrier,
+        // which wave 0 reaches after its reads of this one)
+        v4i *pb = part + buf * (KS * 64);
+        buf ^= 1;
+        pb[wave * 64 + lane] = acc;
+        lds_barrier();
+        if (wave != 0 || r >= M) {
+            if constexpr (kStream) continue;
+            break;
+        }
+        v4i tot = pb[lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) tot += pb[w * 64 + lane];
+        const int t = r;
+        float fs[kMaxSegments];
+        seg_factors(gm, gs, tok_scale[t], fs);
+        const int64_t n0 = tile * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = n0 + 4 * g + i;
+            if (n >= N) continue;
+            const int32_t a = tot[i];
+            const float v = (float)a * seg_pick(gm, fs, n);
+            if constexpr (sizeof(YT) == 4)
+                y[(int64_t)t * N + n] = v;
+            else
+                y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
+            if (acc_out) acc_out[(int64_t)t * N + n] = a;
+        }
+        if constexpr (!kStream) break;  // one tile per block
     }
 }
 
-template <int LAYOUT, int MAXM, int KS, int NSS, typename XT, typename YT>
+template <int LAYOUT, int MAXM, int KS, int NSS, bool STREAM, typename XT, typename YT>
 hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
-                           int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
+                           int64_t N, int64_t K, int64_t grid, YT *y, int32_t *acc,
+                           hipStream_t s) {
     const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
-    const size_t act = (size_t)MAXM * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
-    const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) +
-                        (act > (size_t)KS * 1024 ? act : (size_t)KS * 1024);
-    auto kern = linear_decode_kernel<LAYOUT, KS, NSS, MAXM, XT, YT>;
+    constexpr int64_t kRoundK = (int64_t)KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes;
+    const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (size_t)MAXM * (kRoundK + 16) +
+                        2 * (size_t)KS * 1024;
+    auto kern = linear_decode_kernel<LAYOUT, KS, NSS, MAXM, STREAM, XT, YT>;
     static int lds_raised = 0;
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(64 * KS), smem, s, x, packed,
-                       gamma, (int)M, N, K, rb, y, acc);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS), smem, s, x, packed, gamma,
+                       (int)M, N, K, rb, y, acc);
     return hipGetLastError();
 }
 
-// A one-token specialisation keeps only 16 values of x per thread, which
-// leaves registers for more resident workgroups per CU.
+// One 16-row tile per block, except for several tokens whose rows fit one
+// round (K % 16 == 0) when the tiles outnumber kFusedBlocksPerCu blocks per
+// compute unit: quantising x in every block would then dominate, so the grid
+// is capped there and each block streams several tiles. A one-token
+// specialisation keeps only 16 values of x per thread, which leaves registers
+// for more resident blocks.
 template <int LAYOUT, typename XT, typename YT>
 hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
+    const int64_t tiles = (N + 15) / 16;
+    if (M > 1 && K % 16 == 0 &&
+        K <= (int64_t)kFsKS * kFsNSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes) {
+        const int64_t cap = (int64_t)kFusedBlocksPerCu * device_cu_count();
+        if (cap > 0 && tiles > cap)
+            return launch_linear_m<LAYOUT, kFusedMaxM, kFsKS, kFsNSS, true>(x, packed, gamma, M, N,
+                                                                          K, cap, y, acc, s);
+    }
     if (N >= kWideN) {
-        if (M == 1) return launch_linear_m<LAYOUT, 1, 4, 4>(x, packed, gamma, M, N, K, y, acc, s);
-        return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4>(x, packed, gamma, M, N, K, y, acc, s);
+        if (M == 1)
+            return launch_linear_m<LAYOUT, 1, 4, 4, false>(x, packed, gamma, M, N, K, tiles, y,
+                                                           acc, s);
+        return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4, false>(x, packed, gamma, M, N, K, tiles,
+                                                                y, acc, s);
     }
     if (M == 1)
-        return launch_linear_m<LAYOUT, 1, kFdKS, kFdNSS>(x, packed, gamma, M, N, K, y, acc, s);
-    return launch_linear_m<LAYOUT, kFusedMaxM, kFdKS, kFdNSS>(x, packed, gamma, M, N, K, y, acc, s);
+        return launch_linear_m<LAYOUT, 1, kFdKS, kFdNSS, false>(x, packed, gamma, M, N, K, tiles,
+                                                                y, acc, s);
+    return launch_linear_m<LAYOUT, kFusedMaxM, kFdKS, kFdNSS, false>(x, packed, gamma, M, N, K,
+                                                                     tiles, y, acc, s);
 }
 
 template <int LAYOUT, typename XT>

@@ -292,7 +292,12 @@ def test_zero_activation_row_gives_zero_output(bl):
 @pytest.mark.parametrize("M,N,K,dtype", [(1, 256, 256, "f32"), (2, 100, 1000, "bf16"),
                                          (3, 33, 17, "f32"), (4, 300, 4099, "bf16"),
                                          (1, 4096, 11008, "bf16"), (4, 64, 8192, "f32"),
-                                         (1, 16400, 160, "bf16"), (3, 16384, 5000, "f32")])
+                                         (1, 16400, 160, "bf16"), (3, 16384, 5000, "f32"),
+                                         # several tokens, more 16-row tiles than the
+                                         # capped grid (two blocks per compute unit):
+                                         # blocks stream tiles; ragged last tile
+                                         (2, 8200, 64, "bf16"), (3, 12000, 4096, "f32"),
+                                         (4, 22016, 4096, "bf16"), (2, 9000, 5120, "bf16")])
 def test_fused_linear_parity(bl, layout, M, N, K, dtype):
     """Same activation codes as the stand-alone quantiser (bit-exact), hence
     the same INT32 accumulators as the oracle, and y within tolerance."""

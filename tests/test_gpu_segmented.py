@@ -132,6 +132,26 @@ def test_linear_segmented_parity(bl, layout, M):
 
 
 @pytest.mark.parametrize("layout", ["2bit", "base3"])
+def test_linear_segmented_streaming(bl, layout):
+    """Fused decode of 3 tokens over a stack with more 16-row tiles than the
+    capped grid, so blocks stream tiles across segment boundaries (ragged
+    segments, the last tile partly empty)."""
+    segs, K = (4100, 1030, 3000), 1024
+    M = 3
+    banner(f"linear_segmented streaming {layout} M={M} segs={segs} K={K}")
+    codes, gammas, packed = stacked(segs, K, layout, seed=77)
+    p = synth.make_problem(M=M, N=1, K=K, seed=78, dtype="bf16", outlier_frac=0.01)
+    x = torch.from_numpy(p.x_store.view(np.int16)).cuda().view(torch.bfloat16)
+    y, acc = bl.bitlinear_linear_segmented(x, dev(packed), gpu_gammas(gammas), segs, layout,
+                                           torch.float32, acc=True)
+    torch.cuda.synchronize()
+    xq, scale, _ = oracle.quant_acts(p.x)
+    acc_ref = oracle.int_product(xq, np.concatenate(codes, axis=0))
+    assert np.array_equal(to_np(acc), acc_ref), "INT32 accumulators differ"
+    check_y_f32(to_np(y), ref_y(acc_ref, codes, gammas, scale))
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3"])
 def test_stacked_pack_end_to_end(bl, layout):
     """Q, K, V-like matrices packed one after the other into one buffer, each
     with its gamma written to consecutive floats, then one segmented launch,
