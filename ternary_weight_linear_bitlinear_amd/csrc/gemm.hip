@@ -415,10 +415,11 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
 }
 
 // Tile configuration by problem size, chosen by timing on MI355X: large
-// 2-bit problems use
-// 256 x 256 tiles with 8 waves; when those tiles do not fill whole rounds of
-// 256 CUs, the columns that do are one launch and the leftover columns a
-// second launch with smaller tiles, so no round runs mostly idle.
+// 2-bit problems use 256 x 256 tiles with 8 waves; when those tiles do not
+// fill whole rounds of 256 CUs, the columns that do take 256 x 256 tiles and
+// the leftover columns smaller tiles (in the same launch when they make one
+// round of 256 x 128 tiles, else in a second launch), so no round runs mostly
+// idle.
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
