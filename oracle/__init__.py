@@ -61,6 +61,9 @@ def _load():
         "orc_row_bytes_base3": (_i64, [_i64]),
         "orc_pack_base3": (None, [_p, _i64, _i64, _p]),
         "orc_unpack_base3": (_i64, [_p, _i64, _i64, _p]),
+        "orc_row_bytes_1bit": (_i64, [_i64]),
+        "orc_pack_1bit": (_i64, [_p, _i64, _i64, _p]),
+        "orc_unpack_1bit": (_i64, [_p, _i64, _i64, _p]),
         "orc_quant_acts": (_i64, [_p, _i64, _i64, _p, _p, _p]),
         "orc_int_product": (_i64, [_p, _p, _i64, _i64, _i64, _p]),
         "orc_epilogue": (None, [_p, ctypes.c_float, _p, _i64, _i64, _p]),
@@ -139,16 +142,27 @@ def row_bytes(K: int, layout: str) -> int:
         return int(lib.orc_row_bytes_2bit(K))
     if layout == "base3":
         return int(lib.orc_row_bytes_base3(K))
+    if layout == "1bit":
+        return int(lib.orc_row_bytes_1bit(K))
     raise ValueError(layout)
 
 
+def _layout_fns(layout: str):
+    lib = _load()
+    return {"2bit": (lib.orc_pack_2bit, lib.orc_unpack_2bit),
+            "base3": (lib.orc_pack_base3, lib.orc_unpack_base3),
+            "1bit": (lib.orc_pack_1bit, lib.orc_unpack_1bit)}[layout]
+
+
 def pack(codes: np.ndarray, layout: str) -> np.ndarray:
-    """Pack int8 codes [N, K] into the canonical layout [N, row_bytes]."""
+    """Pack int8 codes [N, K] into the canonical layout [N, row_bytes]. The
+    1-bit layout holds +-1 codes only (ValueError otherwise)."""
     codes = _c(codes, np.int8)
     N, K = codes.shape
     out = np.empty((N, row_bytes(K, layout)), np.uint8)
-    fn = _load().orc_pack_2bit if layout == "2bit" else _load().orc_pack_base3
-    fn(_ptr(codes), N, K, _ptr(out))
+    bad = _layout_fns(layout)[0](_ptr(codes), N, K, _ptr(out))
+    if layout == "1bit" and bad:
+        raise ValueError(f"{bad} codes are not +-1: no 1-bit encoding")
     return out
 
 
@@ -158,8 +172,7 @@ def unpack(packed: np.ndarray, K: int, layout: str) -> tuple[np.ndarray, int]:
     N = packed.shape[0]
     assert packed.shape[1] == row_bytes(K, layout)
     codes = np.empty((N, K), np.int8)
-    fn = _load().orc_unpack_2bit if layout == "2bit" else _load().orc_unpack_base3
-    bad = fn(_ptr(packed), N, K, _ptr(codes))
+    bad = _layout_fns(layout)[1](_ptr(packed), N, K, _ptr(codes))
     return codes, int(bad)
 
 

@@ -201,6 +201,55 @@ int64_t orc_unpack_base3(const uint8_t *packed, int64_t N, int64_t K, int8_t *co
     return bad;
 }
 
+/* 1-bit layout, for the binary (1-bit BitLinear) codes only: [QAT-en] "What
+ * Does BitLinear Change?" stores each +-1 weight in one bit. Bit placement is
+ * not fixed by the pages; reading adopted: bit 1 = +1, bit 0 = -1; codes are
+ * grouped by 32 (one 32-bit little-endian word per group) and code k of the
+ * row lives in
+ *     byte  4*(k/32) + (k%4),   bit  (k%32)/4.
+ * A row occupies roundup(ceil(K/8), 16) bytes; padding bits are 0.          */
+int64_t orc_row_bytes_1bit(int64_t K)
+{
+    int64_t b = (K + 7) / 8;
+    return (b + 15) / 16 * 16;
+}
+
+/* Returns the number of codes that are not +-1 (a ternary 0 has no 1-bit
+ * encoding); they are written as bit 0. */
+int64_t orc_pack_1bit(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed)
+{
+    const int64_t rb = orc_row_bytes_1bit(K);
+    int64_t bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t *row = packed + n * rb;
+        for (int64_t j = 0; j < rb; ++j) row[j] = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int c = codes[n * K + k];
+            if (c != 1 && c != -1) ++bad;
+            if (c == 1) {
+                int64_t byte = 4 * (k / 32) + (k % 4);
+                int bit = (int)((k % 32) / 4);
+                row[byte] = (uint8_t)(row[byte] | (1 << bit));
+            }
+        }
+    }
+    return bad;
+}
+
+/* Every bit pattern is valid; returns 0. */
+int64_t orc_unpack_1bit(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes)
+{
+    const int64_t rb = orc_row_bytes_1bit(K);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t byte = 4 * (k / 32) + (k % 4);
+            int bit = (int)((k % 32) / 4);
+            codes[n * K + k] = (int8_t)(((packed[n * rb + byte] >> bit) & 1) ? 1 : -1);
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Per-token symmetric absmax INT8 activations.
  * [b158] §3.2: scale = max(|x|) per token, x_q = clamp(round(x / scale *

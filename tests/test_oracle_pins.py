@@ -237,6 +237,86 @@ def test_every_base3_byte():
         assert np.array_equal(oracle.pack(codes, "base3"), row)
 
 
+def test_pack_1bit_hand_example():
+    """One 32-code group of +-1 codes, bytes worked out by hand from the
+    layout: code k sits in byte k % 4 at bit k // 4, bit 1 = +1. +1 at k = 0
+    (byte 0 bit 0), 5 (byte 1 bit 1), 10 (byte 2 bit 2), 15 (byte 3 bit 3) and
+    31 (byte 3 bit 7), -1 elsewhere; the rest of the 16-byte row is padding 0."""
+    c = -np.ones((1, 32), np.int8)
+    c[0, [0, 5, 10, 15, 31]] = 1
+    packed = oracle.pack(c, "1bit")
+    assert packed.shape == (1, 16)
+    assert packed[0].tolist() == [0x01, 0x02, 0x04, 0x88] + [0] * 12
+
+
+def test_pack_1bit_word_extraction():
+    """The layout's decode law: for each little-endian 32-bit word (32 codes),
+    (word >> j) & 0x01010101 holds, byte by byte, the bits of codes 4j..4j+3
+    (1 for +1)."""
+    rng = np.random.default_rng(6)
+    c = np.where(rng.random((3, 256)) < 0.5, -1, 1).astype(np.int8)
+    words = oracle.pack(c, "1bit").view("<u4")
+    for n in range(3):
+        for g in range(8):
+            for j in range(8):
+                v = (int(words[n, g]) >> j) & 0x01010101
+                got = [(v >> (8 * b)) & 0xFF for b in range(4)]
+                want = [1 if c[n, 32 * g + 4 * j + b] == 1 else 0 for b in range(4)]
+                assert got == want
+
+
+@pytest.mark.parametrize("K", [1, 7, 8, 9, 31, 32, 33, 127, 128, 129, 1000, 4096])
+def test_pack_1bit_roundtrip(K):
+    rng = np.random.default_rng(K + 1)
+    c = np.where(rng.random((5, K)) < 0.5, -1, 1).astype(np.int8)
+    packed = oracle.pack(c, "1bit")
+    assert packed.shape == (5, ((K + 7) // 8 + 15) // 16 * 16)
+    back, bad = oracle.unpack(packed, K, "1bit")
+    assert bad == 0
+    assert np.array_equal(back, c)
+
+
+def test_every_1bit_byte():
+    """All 256 byte values are valid; byte 0 of a row holds codes 0, 4, ..., 28."""
+    for b in range(256):
+        row = np.zeros((1, 16), np.uint8)
+        row[0, 0] = b
+        codes, bad = oracle.unpack(row, 32, "1bit")
+        assert bad == 0
+        assert [codes[0, 4 * j] for j in range(8)] == [1 if (b >> j) & 1 else -1
+                                                       for j in range(8)]
+        assert np.array_equal(oracle.pack(codes, "1bit"), row)
+
+
+def test_pack_1bit_rejects_ternary_zero():
+    c = np.array([[1, -1, 0, 1]], np.int8)
+    with pytest.raises(ValueError):
+        oracle.pack(c, "1bit")
+
+
+def test_one_bit_storage(golden):
+    """[QAT-en] "What Does BitLinear Change?": +-1 weights take 1 bit each,
+    16x below FP16; rows of a multiple of 128 codes carry no padding."""
+    ex = golden["one_bit_storage"]
+    ratio = ex["bits_per_weight_fp16_printed"] / ex["bits_per_weight_1bit_printed"]
+    for K in (128, 4096, 11008):
+        assert 8 * oracle.row_bytes(K, "1bit") / K == ex["bits_per_weight_1bit_printed"]
+        assert 2 * K / oracle.row_bytes(K, "1bit") == ratio  # FP16 bytes over 1-bit bytes
+
+
+def test_binary_forward_same_in_both_containers():
+    """The 1-bit codes stored in one bit or in the 2-bit container unpack to the
+    same codes, so the whole forward pass agrees."""
+    rng = np.random.default_rng(8)
+    w = rng.normal(0, 0.02, size=(40, 300)).astype(np.float32)
+    x = rng.normal(0, 1, size=(3, 300)).astype(np.float32)
+    a = oracle.forward(w, x, "1bit", "binary")
+    b = oracle.forward(w, x, "2bit", "binary")
+    assert np.array_equal(oracle.unpack(a["packed"], 300, "1bit")[0],
+                          oracle.unpack(b["packed"], 300, "2bit")[0])
+    assert np.array_equal(a["acc"], b["acc"]) and np.array_equal(a["y64"], b["y64"])
+
+
 def test_storage_arithmetic(golden):
     """[b158] §4.1: 70B weights take 140 GB in FP16, 17.5 GB at 2 bits and about
     14 GB at five per byte; 1.6 bits per weight, about 10x below FP16."""
