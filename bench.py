@@ -149,8 +149,11 @@ def main():
     xs = [to_dev(synth.make_problem(M=1, N=1, K=p.K, seed=1000 + r, dtype="bf16",
                                     outlier_frac=0.01).x_store, True) for r in range(R)]
     decode = {}
-    for layout in ("2bit", "base3"):
-        packed, gamma = bl.bitlinear_pack_weights(W, layout)
+    # ternary codes in the 2-bit and base-3 layouts; the 1-bit variant's
+    # binary codes of the same W in the 1-bit layout
+    for layout in ("2bit", "base3", "1bit"):
+        scheme = "binary" if layout == "1bit" else "ternary"
+        packed, gamma = bl.bitlinear_pack_weights(W, layout, scheme)
         copies = [packed.clone() for _ in range(R)]
         y = torch.empty((1, p.N), dtype=torch.float32, device=dev)
         xq = torch.empty((1, p.K), dtype=torch.int8, device=dev)
@@ -190,7 +193,7 @@ def main():
         lut_ms = graph_ms(gemv_lut, 2 * R) if layout == "base3" else None
         # fused kernel: packed weights + bf16 x + gamma + fp32 y
         alg = wbytes + 2 * p.K + 4 + 4 * p.N
-        decode[layout] = dict(ms_per_step=ms_step, weight_bytes=wbytes,
+        decode[layout] = dict(scheme=scheme, ms_per_step=ms_step, weight_bytes=wbytes,
                               weight_gbs=wbytes / (ms_step * 1e-3) / 1e9,
                               fused_alg_bytes=alg,
                               fused_gbs=alg / (ms_step * 1e-3) / 1e9,
@@ -201,7 +204,8 @@ def main():
             # the same product by activation-side lookup tables (comparison)
             decode[layout]["lookup_table_forward_ms"] = lut_ms
             decode[layout]["lookup_table_forward_gbs"] = wbytes / (lut_ms * 1e-3) / 1e9
-        log(f"decode {layout}: fused step {ms_step*1e3:.2f} us ({decode[layout]['fused_gbs']:.0f} GB/s), "
+        log(f"decode {layout} ({scheme}): fused step {ms_step*1e3:.2f} us "
+            f"({decode[layout]['fused_gbs']:.0f} GB/s), "
             f"two-launch step {ms_two*1e3:.2f} us, forward only {k_mean*1e3:.2f} us"
             + (f", lookup-table forward {lut_ms*1e3:.2f} us" if lut_ms is not None else ""))
         del copies
@@ -213,30 +217,35 @@ def main():
     # shape of a vocabulary projection), 16 rotating copies.
     if want("stream"):
         ps = synth.make_problem(M=1, N=32768, K=4096, seed=9, dtype="bf16", outlier_frac=0.01)
-        pk, g = bl.bitlinear_pack_weights(to_dev(ps.w_store, True), "2bit")
-        cps = [pk.clone() for _ in range(16)]
+        Ws = to_dev(ps.w_store, True)
         xs1 = to_dev(ps.x_store, True)
         ys = torch.empty((1, ps.N), dtype=torch.float32, device=dev)
-        f = lambda i: bl.bitlinear_linear(xs1, cps[i % 16], g, ps.N, "2bit", y=ys)
-        ms = graph_ms(f, 64)
-        alg = pk.numel() + 2 * ps.K + 4 + 4 * ps.N
-        rows["decode_stream_32768x4096"] = dict(ms=ms, alg_bytes=alg,
-                                               gbs=alg / (ms * 1e-3) / 1e9,
-                                               frac_hbm=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
-        log(f"stream 32768x4096: {ms*1e3:.2f} us = {alg/(ms*1e-3)/1e9:.0f} GB/s")
-        del cps
+        for layout, scheme, key in (("2bit", "ternary", "decode_stream_32768x4096"),
+                                    ("1bit", "binary", "decode_stream_32768x4096_1bit")):
+            pk, g = bl.bitlinear_pack_weights(Ws, layout, scheme)
+            cps = [pk.clone() for _ in range(16)]
+            f = lambda i, cps=cps, g=g, layout=layout: bl.bitlinear_linear(
+                xs1, cps[i % 16], g, ps.N, layout, y=ys)
+            ms = graph_ms(f, 64)
+            alg = pk.numel() + 2 * ps.K + 4 + 4 * ps.N
+            rows[key] = dict(ms=ms, alg_bytes=alg, gbs=alg / (ms * 1e-3) / 1e9,
+                             frac_hbm=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            log(f"stream 32768x4096 {layout}: {ms*1e3:.2f} us = {alg/(ms*1e-3)/1e9:.0f} GB/s")
+            del cps
+        del Ws
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ pack
     if want("pack"):
         ws = torch.empty(bl.bitlinear_pack_workspace_bytes(p.N, p.K), dtype=torch.uint8, device=dev)
         pk = {}
-        for layout in ("2bit", "base3"):
+        for layout in ("2bit", "base3", "1bit"):
+            scheme = "binary" if layout == "1bit" else "ternary"
             packed = torch.empty((p.N, bl.bitlinear_packed_row_bytes(p.K, layout)),
                                  dtype=torch.uint8, device=dev)
             g = torch.empty(4, dtype=torch.float32, device=dev)[:1]
-            f = lambda i, layout=layout, packed=packed, g=g: bl.bitlinear_pack_weights(
-                W, layout, packed=packed, gamma=g, workspace=ws)
+            f = lambda i, layout=layout, scheme=scheme, packed=packed, g=g: \
+                bl.bitlinear_pack_weights(W, layout, scheme, packed=packed, gamma=g, workspace=ws)
             ms = graph_ms(f, 20)
             byt = 2 * p.N * p.K * 2 + packed.numel()  # W read by both passes + codes written
             pk[layout] = dict(ms=ms, gbs=byt / (ms * 1e-3) / 1e9)
@@ -254,8 +263,9 @@ def main():
         pre = {"quant_acts_ms": qa_ms,
                "quant_acts_gbs": (q.M * q.K * 3 + 4 * q.M) / (qa_ms * 1e-3) / 1e9}
         ops = 2.0 * q.M * q.N * q.K
-        for layout in ("2bit", "base3"):
-            packed, gamma = bl.bitlinear_pack_weights(Wp, layout)
+        for layout in ("2bit", "base3", "1bit"):
+            packed, gamma = bl.bitlinear_pack_weights(Wp, layout,
+                                                      "binary" if layout == "1bit" else "ternary")
             y = torch.empty((q.M, q.N), dtype=torch.bfloat16, device=dev)
             f = lambda i, packed=packed, gamma=gamma, layout=layout, y=y: bl.bitlinear_forward(
                 xq, sc, packed, gamma, q.N, q.K, layout, torch.bfloat16, y=y)

@@ -69,8 +69,15 @@ typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
  * BL_PACK_BASE3: byte j of a row holds codes 5j..5j+4 as the base-3 number
  *   t0 + 3 t1 + 9 t2 + 27 t3 + 81 t4 with t = c + 1 (first code in the least
  *   significant trit; values 0..242). row_bytes = roundup(ceil(K/5), 16);
- *   padding trits are t = 1 (code 0). */
-typedef enum { BL_PACK_2BIT = 0, BL_PACK_BASE3 = 1 } bl_layout;
+ *   padding trits are t = 1 (code 0).
+ * BL_PACK_1BIT: binary codes only (BL_BINARY), one bit per weight as in the
+ *   1-bit BitLinear ([QAT-en] "What Does BitLinear Change?": +-1 weights at
+ *   1 bit each). Bit 1 = +1, bit 0 = -1. Codes are grouped by 32 into one
+ *   little-endian 32-bit word; code k of a row sits in byte 4*(k/32) + (k%4)
+ *   at bit (k%32)/4, so that (word >> j) & 0x01010101 holds codes 4j..4j+3 in
+ *   its four bytes. row_bytes = roundup(ceil(K/8), 16); padding bits are 0
+ *   (the products never read them). Every bit pattern is a valid matrix. */
+typedef enum { BL_PACK_2BIT = 0, BL_PACK_BASE3 = 1, BL_PACK_1BIT = 2 } bl_layout;
 
 /* Weight quantisers.
  * BL_TERNARY (b1.58): gamma = mean|W|; c = clamp(round(W / (gamma + eps)),
@@ -101,7 +108,9 @@ size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
  *             It stays on the device; no host synchronisation happens.
  *   workspace device scratch of at least bitlinear_pack_workspace_bytes(N, K)
  *             bytes; its contents are overwritten.
- * The mean is accumulated in fp64 and rounded once to fp32. */
+ * The mean is accumulated in fp64 and rounded once to fp32. Layout
+ * BL_PACK_1BIT holds binary codes only: BL_TERNARY with it returns
+ * BL_ERR_INVALID_ARG. */
 bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K,
                                  int scheme, int layout, float eps,
                                  uint8_t *packed, float *gamma,
@@ -198,8 +207,8 @@ bl_status bitlinear_forward_lut(const int8_t *xq, const float *scale, const uint
  *   packed  [N, row_bytes] codes in BL_PACK_2BIT (the forward's own matrix; no
  *           transposed copy is needed); gamma: 1 float (device).
  *   grad_x  out: [M, K] fp32.
- * Requires N % 8 == 0. BL_F32 grad_y, BL_PACK_BASE3 or other N return
- * BL_ERR_UNSUPPORTED. Dimensions above 2^24 return BL_ERR_INVALID_ARG.
+ * Requires N % 8 == 0. BL_F32 grad_y, BL_PACK_BASE3, BL_PACK_1BIT or other N
+ * return BL_ERR_UNSUPPORTED. Dimensions above 2^24 return BL_ERR_INVALID_ARG.
  * M = 0 is a no-op; N = 0 writes zeros. */
 bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,
                                    int layout, const float *gamma, int64_t M, int64_t N,

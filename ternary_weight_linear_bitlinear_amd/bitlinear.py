@@ -21,10 +21,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitlinea
 
 BL_OK, BL_ERR_INVALID_ARG, BL_ERR_UNSUPPORTED, BL_ERR_DEVICE = 0, 1, 2, 3
 BL_F32, BL_BF16 = 0, 1
-BL_PACK_2BIT, BL_PACK_BASE3 = 0, 1
+BL_PACK_2BIT, BL_PACK_BASE3, BL_PACK_1BIT = 0, 1, 2
 BL_TERNARY, BL_BINARY = 0, 1
 
-LAYOUTS = {"2bit": BL_PACK_2BIT, "base3": BL_PACK_BASE3}
+LAYOUTS = {"2bit": BL_PACK_2BIT, "base3": BL_PACK_BASE3, "1bit": BL_PACK_1BIT}
 SCHEMES = {"ternary": BL_TERNARY, "binary": BL_BINARY}
 _DTYPES = {torch.float32: BL_F32, torch.bfloat16: BL_BF16}
 

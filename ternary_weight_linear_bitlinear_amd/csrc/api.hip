@@ -24,7 +24,10 @@ std::atomic<int> g_arch[kMaxDevices];
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool valid_dtype(int d) { return d == BL_F32 || d == BL_BF16; }
-bool valid_layout(int l) { return l == BL_PACK_2BIT || l == BL_PACK_BASE3; }
+bool valid_layout(int l) { return l == BL_PACK_2BIT || l == BL_PACK_BASE3 || l == BL_PACK_1BIT; }
+static_assert(BL_PACK_2BIT == bl::kLayout2Bit && BL_PACK_BASE3 == bl::kLayoutBase3 &&
+                  BL_PACK_1BIT == bl::kLayout1Bit,
+              "layout numbering");
 bool valid_scheme(int s) { return s == BL_TERNARY || s == BL_BINARY; }
 
 bl_status device_ok() {
@@ -54,9 +57,7 @@ bl_status launched(hipError_t e) {
     return BL_OK;
 }
 
-int64_t row_bytes(int64_t K, int layout) {
-    return layout == BL_PACK_2BIT ? bl::row_bytes_2bit(K) : bl::row_bytes_base3(K);
-}
+int64_t row_bytes(int64_t K, int layout) { return bl::row_bytes_of(layout, K); }
 
 // Segment table of a stacked matrix: 1..kMaxSegments host row counts, each
 // >= 1. Fills `gm` (bounds = running row totals) and `N` (the total).
@@ -137,6 +138,7 @@ bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t 
     if (N > INT64_MAX / K) return BL_ERR_INVALID_ARG;
     if (!valid_dtype(w_dtype) || !valid_layout(layout) || !valid_scheme(scheme))
         return BL_ERR_INVALID_ARG;
+    if (layout == BL_PACK_1BIT && scheme != BL_BINARY) return BL_ERR_INVALID_ARG;
     if (!std::isfinite(eps) || eps < 0.f) return BL_ERR_INVALID_ARG;
     if (workspace_bytes < bl::pack_workspace_bytes(N * K)) return BL_ERR_INVALID_ARG;
     bl_status st = device_ok();

@@ -14,6 +14,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kLayout2Bit = 0;
 constexpr int kLayoutBase3 = 1;
+constexpr int kLayout1Bit = 2;  // binary codes only
 constexpr int kSchemeTernary = 0;
 constexpr int kSchemeBinary = 1;
 constexpr int kF32 = 0;
@@ -74,6 +75,12 @@ struct GammaMap {
 
 inline int64_t row_bytes_2bit(int64_t K) { return ((K + 3) / 4 + 15) / 16 * 16; }
 inline int64_t row_bytes_base3(int64_t K) { return ((K + 4) / 5 + 15) / 16 * 16; }
+inline int64_t row_bytes_1bit(int64_t K) { return ((K + 7) / 8 + 15) / 16 * 16; }
+inline int64_t row_bytes_of(int layout, int64_t K) {
+    return layout == kLayout2Bit    ? row_bytes_2bit(K)
+           : layout == kLayoutBase3 ? row_bytes_base3(K)
+                                    : row_bytes_1bit(K);
+}
 
 // ---- weight quantisation (quant.hip) -------------------------------------
 // Number of partial sums the mean reduction writes for `count` elements.

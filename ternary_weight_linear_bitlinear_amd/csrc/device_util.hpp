@@ -154,6 +154,19 @@ __device__ __forceinline__ void expand_2bit_word(uint32_t w, int out[4]) {
     }
 }
 
+// 1-bit layout: bit j of byte i of a 32-code word is code 4j + i (1 = +1).
+// Codes 16h .. 16h + 15 of the word (h = 0, 1) as four words of signed bytes:
+// (w >> (4h + t)) & 0x01010101 selects byte 0 (-1) or byte 1 (+1) of the
+// table 0x000001FF for codes 16h + 4t .. +3.
+__device__ __forceinline__ void expand_1bit_half(uint32_t w, int h, int out[4]) {
+    constexpr uint32_t kTable = 0x000001FFu;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t b = (w >> (4 * h + t)) & 0x01010101u;
+        out[t] = (int)__builtin_amdgcn_perm(0u, kTable, b);
+    }
+}
+
 // Base-3 decode table: entry v (0..242) holds the five signed codes t_i - 1
 // of v = sum t_i 3^i in bytes 0..4 (bytes 5..7 zero); entries 243..255 are
 // zero. Built once per workgroup into LDS from this arithmetic definition.

@@ -5,15 +5,16 @@
 // instruction is v_mfma_i32_32x32x32_i8.
 //
 // Data flow. Activations (int8) are staged through LDS, double buffered.
-// Packed weight codes never touch LDS: each wave loads the 16-byte packed
-// units of its own fragment columns straight from global memory (L2) and
-// expands them in registers to signed code bytes. The k slots of an MFMA are
-// a free choice as long as both operands agree, so within one k-tile of two
-// packed units per weight row (128 codes in the 2-bit layout, 160 in base-3)
-// lane group g (lanes 32g..32g+31) takes unit g, and MFMA k-step s takes
-// codes [UC*g + 16 s, +16) of the tile for that lane group (UC = codes per
-// unit); one 16-byte load then feeds all 4 (5) k-steps of the tile, and the
-// activation operand is read from LDS at the same offsets.
+// Packed weight codes never touch LDS: each wave loads the packed units of
+// its own fragment columns straight from global memory (L2) and expands them
+// in registers to signed code bytes. A unit is 16 bytes (64 codes in the
+// 2-bit layout, 80 in base-3) or 8 bytes (64 codes in the 1-bit layout). The
+// k slots of an MFMA are a free choice as long as both operands agree, so
+// within one k-tile of two units per weight row (128 or 160 codes) lane group
+// g (lanes 32g..32g+31) takes unit g, and MFMA k-step s takes codes
+// [UC*g + 16 s, +16) of the tile for that lane group (UC = codes per unit);
+// one load then feeds all 4 (5) k-steps of the tile, and the activation
+// operand is read from LDS at the same offsets.
 //
 // Block tile BM tokens x BN weight rows, WM x WN waves, each owning
 // (BM/WM) x (BN/WN) outputs as 32 x 32 fragments. Loads run two k-tiles ahead
@@ -35,7 +36,8 @@ struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int DIST = DIST_;  // k-tiles the global loads run ahead (1 or 2)
     static constexpr int kThreads = 64 * WM * WN;
-    static constexpr int UC = LAYOUT == kLayout2Bit ? 64 : 80;  // codes per 16-byte unit
+    static constexpr int UC = LAYOUT == kLayoutBase3 ? 80 : 64;  // codes per unit
+    static constexpr int LB = LAYOUT == kLayout1Bit ? 8 : 16;     // bytes per unit
     static constexpr int BK = 2 * UC;                             // codes per k-tile
     static constexpr int LDSK = BK + 16;                          // padded LDS row (bytes)
     static constexpr int KSTEPS = UC / 16;                        // MFMA k-steps per tile
@@ -70,6 +72,17 @@ __device__ __forceinline__ void expand_unit(const uint4 wv, const uint64_t *lut,
         }
 #pragma unroll
         for (int i = 0; i < 20; ++i) c[i] = (int)d[i];
+    }
+}
+
+// One unit of packed codes (16 bytes; 8 bytes in the 1-bit layout).
+template <int LAYOUT>
+__device__ __forceinline__ uint4 load_b(const uint8_t *p) {
+    if constexpr (LAYOUT == kLayout1Bit) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        return make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        return *reinterpret_cast<const uint4 *>(p);
     }
 }
 
@@ -127,7 +140,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
             lut[i] = base3_entry((uint32_t)(i % 256)) << (8 * (i / 256));
     }
 
-    const int64_t units = rb / 16;
+    const int64_t units = rb / C::LB;
     const int64_t ktiles = (units + 1) / 2;
     // this lane's weight rows (one per fragment column block)
     const uint8_t *b_src[C::FJ];
@@ -183,11 +196,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
             if (!G) {
-                b_reg[j] = *reinterpret_cast<const uint4 *>(b_src[j] + unit * 16);
+                b_reg[j] = load_b<LAYOUT>(b_src[j] + unit * C::LB);
             } else {
                 const bool ok = b_ok[j] && unit < units;
-                const uint4 v =
-                    *reinterpret_cast<const uint4 *>(b_src[j] + (ok ? unit * 16 : 0));
+                const uint4 v = load_b<LAYOUT>(b_src[j] + (ok ? unit * C::LB : 0));
                 b_reg[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -243,6 +255,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
                                                                                      : bu[j].w;
                     int c[4];
                     expand_2bit_word(w, c);
+                    bj = v4i{c[0], c[1], c[2], c[3]};
+                } else if constexpr (LAYOUT == kLayout1Bit) {
+                    // k-step ks: codes 16 ks .. +15 of the unit = half ks % 2
+                    // of word ks / 2
+                    int c[4];
+                    expand_1bit_half(ks < 2 ? bu[j].x : bu[j].y, ks % 2, c);
                     bj = v4i{c[0], c[1], c[2], c[3]};
                 } else {
                     bj = v4i{cb[j][4 * ks], cb[j][4 * ks + 1], cb[j][4 * ks + 2],
@@ -398,7 +416,7 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                             int64_t ldy, int32_t *acc, hipStream_t s) {
     using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
-    const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
+    const int64_t rb = row_bytes_of(LAYOUT, K);
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const int64_t ntiles = (int64_t)tm * tn;
     const int64_t blocks = (ntiles + kXcds - 1) / kXcds * kXcds;
@@ -440,7 +458,7 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
 }
 
 // Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in 256 x 128 tiles,
-// one launch (2-bit).
+// one launch (2-bit and 1-bit).
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t n_main,
@@ -448,7 +466,7 @@ hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t 
     using C1 = GemmCfg<LAYOUT, 256, 256, 2, 4, 2>;
     using C2 = GemmCfg<LAYOUT, 256, 128, 2, 4, 2>;
     static_assert(C1::SMEM == C2::SMEM && C1::kThreads == C2::kThreads, "one launch shape");
-    const int64_t rb = row_bytes_2bit(K);
+    const int64_t rb = row_bytes_of(LAYOUT, K);
     const int tm = (int)((M + 255) / 256);
     const int tn1 = (int)((n_main + 255) / 256), tn2 = (int)((N - n_main + 127) / 128);
     const GemmArgs<YT> g1{xq, scale, packed, gamma, M, n_main, K, rb, tm, tn1, y, N, acc};
@@ -473,8 +491,8 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
                          const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                          int32_t *acc, hipStream_t s) {
     constexpr int64_t kCUs = 256;
-    const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
-    if constexpr (LAYOUT == kLayout2Bit) {
+    const int64_t rb = row_bytes_of(LAYOUT, K);
+    if constexpr (LAYOUT != kLayoutBase3) {
         const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
         if (tm * tn >= kCUs) {
             // columns covered by whole rounds of 256 x 256 tiles
@@ -504,18 +522,19 @@ hipError_t launch_forward_gemm(const int8_t *xq, const float *scale, const uint8
                                int layout, const GammaMap &gamma, int64_t M, int64_t N, int64_t K,
                                void *y, int y_dtype, int32_t *acc, hipStream_t stream) {
     if (M > (int64_t)2147483647 || N > (int64_t)2147483647) return hipErrorInvalidValue;
-    if (layout == kLayout2Bit) {
+    auto go = [&](auto layout_c) {
+        constexpr int L = decltype(layout_c)::value;
         if (y_dtype == kF32)
-            return launch_gemm_t<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
-                                              static_cast<float *>(y), acc, stream);
-        return launch_gemm_t<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
-                                          static_cast<uint16_t *>(y), acc, stream);
+            return launch_gemm_t<L>(xq, scale, packed, gamma, M, N, K, static_cast<float *>(y),
+                                    acc, stream);
+        return launch_gemm_t<L>(xq, scale, packed, gamma, M, N, K, static_cast<uint16_t *>(y),
+                                acc, stream);
+    };
+    switch (layout) {
+        case kLayout2Bit: return go(std::integral_constant<int, kLayout2Bit>{});
+        case kLayoutBase3: return go(std::integral_constant<int, kLayoutBase3>{});
+        default: return go(std::integral_constant<int, kLayout1Bit>{});
     }
-    if (y_dtype == kF32)
-        return launch_gemm_t<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
-                                           static_cast<float *>(y), acc, stream);
-    return launch_gemm_t<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
-                                       static_cast<uint16_t *>(y), acc, stream);
 }
 
 }  // namespace bl

@@ -214,6 +214,36 @@ __global__ __launch_bounds__(kThreads) void pack_base3_kernel(
     }
 }
 
+// Pass 2, 1-bit layout (binary codes only; [QAT-en] "What Does BitLinear
+// Change?" stores each +-1 weight in one bit): one thread writes 8 bytes = 64
+// codes, i.e. two 32-code words; word q, byte i, bit j holds code 32q + 4j + i,
+// 1 for +1. Padding bits are 0.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void pack_1bit_kernel(
+    const T *__restrict__ w, int64_t N, int64_t K, int64_t rb,
+    const double2 *__restrict__ parts, int nparts, float eps,
+    uint8_t *__restrict__ packed, float *__restrict__ gamma_out) {
+    const CodeRule<kSchemeBinary> rule =
+        make_rule<kSchemeBinary>(parts, nparts, N * K, eps, gamma_out);
+    const int64_t halves_per_row = rb / 8;
+    const int64_t halves = N * halves_per_row;
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < halves;
+         u += (int64_t)gridDim.x * kThreads) {
+        const int64_t row = u / halves_per_row;
+        const int64_t k0 = (u % halves_per_row) * 64;
+        float v[64];
+        const int valid = load_run<T, 64>(w, row, K, k0, v);
+        uint32_t word[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+            const uint32_t bit = e < valid && rule.u_of(v[e]) == 2 ? 1u : 0u;
+            const int q = e / 32, j = (e % 32) / 4, i = e % 4;
+            word[q] |= bit << (8 * i + j);
+        }
+        *reinterpret_cast<uint2 *>(packed + row * rb + (k0 / 8)) = make_uint2(word[0], word[1]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Per-token INT8 quantisation. One block per token row; thread t owns the
 // 8-element chunks t, t + 256, ..., kept in registers between the max
@@ -321,12 +351,16 @@ hipError_t pack_t(const T *w, int64_t N, int64_t K, int scheme, int layout, floa
     double2 *parts = reinterpret_cast<double2 *>(ws);
     hipLaunchKernelGGL((absmean_partial_kernel<T>), dim3(nparts), dim3(kThreads), 0, s, w,
                        count, parts);
-    const int64_t rb = layout == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
-    const int64_t units = N * (rb / 16);
+    const int64_t rb = row_bytes_of(layout, K);
+    // one thread per 16-byte unit (8 bytes in the 1-bit layout)
+    const int64_t units = N * (rb / (layout == kLayout1Bit ? 8 : 16));
     int64_t blocks = (units + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
     dim3 grid((unsigned)blocks), block(kThreads);
-    if (layout == kLayout2Bit) {
+    if (layout == kLayout1Bit) {  // binary codes only (the API checks the scheme)
+        hipLaunchKernelGGL((pack_1bit_kernel<T>), grid, block, 0, s, w, N, K, rb, parts, nparts,
+                           eps, packed, gamma);
+    } else if (layout == kLayout2Bit) {
         if (scheme == kSchemeTernary)
             hipLaunchKernelGGL((pack_2bit_kernel<T, kSchemeTernary>), grid, block, 0, s, w, N, K,
                                rb, parts, nparts, eps, packed, gamma);

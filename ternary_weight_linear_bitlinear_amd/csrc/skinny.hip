@@ -54,20 +54,39 @@ __device__ __forceinline__ void unpack_raw(const uint4 (&p)[4], float v[16]) {
     }
 }
 
+// A unit is what one lane loads per row: 16 bytes of 2-bit (64 codes) or
+// base-3 (80 codes) codes, 8 bytes of 1-bit codes (64 codes), so that every
+// layout feeds the same 16-code matrix-core steps.
 template <int LAYOUT>
 struct SkinnyCfg {
-    static constexpr int kUnitCodes = LAYOUT == kLayout2Bit ? 64 : 80;
+    static constexpr int kUnitCodes = LAYOUT == kLayoutBase3 ? 80 : 64;
+    static constexpr int kUnitBytes = LAYOUT == kLayout1Bit ? 8 : 16;
     static constexpr int kSteps = kUnitCodes / 16;  // MFMA instructions per unit
 };
 
-// Decode one 16-byte unit into signed code bytes (natural k order).
+template <int LAYOUT>
+__device__ __forceinline__ uint4 load_unit(const uint8_t *p) {
+    if constexpr (LAYOUT == kLayout1Bit) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        return make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        return *reinterpret_cast<const uint4 *>(p);
+    }
+}
+
+// Decode one unit into signed code bytes (natural k order).
 template <int LAYOUT>
 __device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut, int c[20]) {
-    if (LAYOUT == kLayout2Bit) {
+    if constexpr (LAYOUT == kLayout2Bit) {
         expand_2bit_word(wv.x, c + 0);
         expand_2bit_word(wv.y, c + 4);
         expand_2bit_word(wv.z, c + 8);
         expand_2bit_word(wv.w, c + 12);
+    } else if constexpr (LAYOUT == kLayout1Bit) {
+        expand_1bit_half(wv.x, 0, c + 0);
+        expand_1bit_half(wv.x, 1, c + 4);
+        expand_1bit_half(wv.y, 0, c + 8);
+        expand_1bit_half(wv.y, 1, c + 12);
     } else {
         uint32_t d[20];
 #pragma unroll
@@ -126,7 +145,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
             lut[i] = base3_entry((uint32_t)(i % 256)) << (8 * (i / 256));
     }
 
-    const int64_t units = rb / 16;
+    const int64_t units = rb / C::kUnitBytes;
     const bool aligned = (K % 16) == 0;
     const int chunks = M * kChunksPerTok;
     const uint8_t *wrow[RG];
@@ -168,8 +187,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
             for (int s = 0; s < NSS; ++s) {
                 const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
                 wok[q][s] = row_ok[q] && unit < units;
-                wv[q][s] =
-                    *reinterpret_cast<const uint4 *>(wok[q][s] ? wrow[q] + unit * 16 : packed);
+                wv[q][s] = load_unit<LAYOUT>(wok[q][s] ? wrow[q] + unit * C::kUnitBytes : packed);
             }
         // 3. stage the activations in LDS (zero past K)
         lds_barrier();  // previous round's readers are done
@@ -252,7 +270,7 @@ template <int LAYOUT, int KS, int NSS, int RG, int MAXM, typename YT>
 hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *packed,
                            const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int32_t *acc, hipStream_t s) {
-    const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
+    const int64_t rb = row_bytes_of(LAYOUT, K);
     // the partial-tile buffer aliases the activation area (needs KS*RG KiB)
     const size_t act = (size_t)M * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
     const size_t part = (size_t)KS * RG * 1024;
@@ -328,7 +346,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const int r = lane % 16;
     const int g = lane / 16;
     const int64_t tiles = (N + 15) / 16;  // 16 weight rows per tile
-    const int64_t units = rb / 16;
+    const int64_t units = rb / C::kUnitBytes;
     const bool vec = (K % 8) == 0;
 
     float gs[kMaxSegments];
@@ -345,7 +363,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
             ok[s] = n < N && unit < units;
             // out-of-range lanes read a valid address; the value is zeroed
             // where it is consumed, so no wait is forced here
-            w[s] = *reinterpret_cast<const uint4 *>(ok[s] ? wrow + unit * 16 : packed);
+            w[s] = load_unit<LAYOUT>(ok[s] ? wrow + unit * C::kUnitBytes : packed);
         }
     };
 
@@ -565,7 +583,7 @@ template <int LAYOUT, int MAXM, int KS, int NSS, bool STREAM, typename XT, typen
 hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, int64_t grid, YT *y, int32_t *acc,
                            hipStream_t s) {
-    const int64_t rb = LAYOUT == kLayout2Bit ? row_bytes_2bit(K) : row_bytes_base3(K);
+    const int64_t rb = row_bytes_of(LAYOUT, K);
     constexpr int64_t kRoundK = (int64_t)KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes;
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (size_t)MAXM * (kRoundK + 16) +
                         2 * (size_t)KS * 1024;
@@ -618,46 +636,62 @@ hipError_t launch_linear_x(const XT *x, const uint8_t *packed, const GammaMap &g
     return launch_linear_t<LAYOUT>(x, packed, gamma, M, N, K, static_cast<uint16_t *>(y), acc, s);
 }
 
+template <int LAYOUT>
+hipError_t skinny_y(const int8_t *xq, const float *scale, const uint8_t *packed,
+                    const GammaMap &gamma, int64_t M, int64_t N, int64_t K, void *y, int y_dtype,
+                    int32_t *acc, hipStream_t stream) {
+    if (y_dtype == kF32)
+        return launch_skinny_l<LAYOUT>(xq, scale, packed, gamma, M, N, K, static_cast<float *>(y),
+                                       acc, stream);
+    return launch_skinny_l<LAYOUT>(xq, scale, packed, gamma, M, N, K, static_cast<uint16_t *>(y),
+                                   acc, stream);
+}
+
+template <int LAYOUT>
+hipError_t linear_xy(const void *x, int x_dtype, const uint8_t *packed, const GammaMap &gamma,
+                     int64_t M, int64_t N, int64_t K, void *y, int y_dtype, int32_t *acc,
+                     hipStream_t stream) {
+    if (x_dtype == kF32)
+        return launch_linear_x<LAYOUT>(static_cast<const float *>(x), packed, gamma, M, N, K, y,
+                                       y_dtype, acc, stream);
+    return launch_linear_x<LAYOUT>(static_cast<const uint16_t *>(x), packed, gamma, M, N, K, y,
+                                   y_dtype, acc, stream);
+}
+
 }  // namespace
 
 hipError_t launch_forward_skinny(const int8_t *xq, const float *scale, const uint8_t *packed,
                                  int layout, const GammaMap &gamma, int64_t M, int64_t N, int64_t K,
                                  void *y, int y_dtype, int32_t *acc, hipStream_t stream) {
-    if (layout == kLayout2Bit) {
-        if (y_dtype == kF32)
-            return launch_skinny_l<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
-                                                static_cast<float *>(y), acc, stream);
-        return launch_skinny_l<kLayout2Bit>(xq, scale, packed, gamma, M, N, K,
-                                            static_cast<uint16_t *>(y), acc, stream);
+    switch (layout) {
+        case kLayout2Bit:
+            return skinny_y<kLayout2Bit>(xq, scale, packed, gamma, M, N, K, y, y_dtype, acc,
+                                         stream);
+        case kLayoutBase3:
+            return skinny_y<kLayoutBase3>(xq, scale, packed, gamma, M, N, K, y, y_dtype, acc,
+                                          stream);
+        default:
+            return skinny_y<kLayout1Bit>(xq, scale, packed, gamma, M, N, K, y, y_dtype, acc,
+                                         stream);
     }
-    if (y_dtype == kF32)
-        return launch_skinny_l<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
-                                             static_cast<float *>(y), acc, stream);
-    return launch_skinny_l<kLayoutBase3>(xq, scale, packed, gamma, M, N, K,
-                                         static_cast<uint16_t *>(y), acc, stream);
 }
-
-}  // namespace bl
-
-namespace bl {
 
 int64_t fused_decode_max_m() { return kFusedMaxM; }
 
 hipError_t launch_linear_decode(const void *x, int x_dtype, const uint8_t *packed, int layout,
                                 const GammaMap &gamma, int64_t M, int64_t N, int64_t K, void *y,
                                 int y_dtype, int32_t *acc, hipStream_t stream) {
-    if (layout == kLayout2Bit) {
-        if (x_dtype == kF32)
-            return launch_linear_x<kLayout2Bit>(static_cast<const float *>(x), packed, gamma, M,
-                                                N, K, y, y_dtype, acc, stream);
-        return launch_linear_x<kLayout2Bit>(static_cast<const uint16_t *>(x), packed, gamma, M, N,
-                                            K, y, y_dtype, acc, stream);
+    switch (layout) {
+        case kLayout2Bit:
+            return linear_xy<kLayout2Bit>(x, x_dtype, packed, gamma, M, N, K, y, y_dtype, acc,
+                                          stream);
+        case kLayoutBase3:
+            return linear_xy<kLayoutBase3>(x, x_dtype, packed, gamma, M, N, K, y, y_dtype, acc,
+                                           stream);
+        default:
+            return linear_xy<kLayout1Bit>(x, x_dtype, packed, gamma, M, N, K, y, y_dtype, acc,
+                                          stream);
     }
-    if (x_dtype == kF32)
-        return launch_linear_x<kLayoutBase3>(static_cast<const float *>(x), packed, gamma, M, N,
-                                             K, y, y_dtype, acc, stream);
-    return launch_linear_x<kLayoutBase3>(static_cast<const uint16_t *>(x), packed, gamma, M, N, K,
-                                         y, y_dtype, acc, stream);
 }
 
 }  // namespace bl

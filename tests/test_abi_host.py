@@ -43,10 +43,12 @@ def test_row_bytes(bl):
     for K in [1, 3, 4, 5, 16, 63, 64, 65, 79, 80, 81, 4096, 11008]:
         assert bl.bitlinear_packed_row_bytes(K, "2bit") == oracle.row_bytes(K, "2bit")
         assert bl.bitlinear_packed_row_bytes(K, "base3") == oracle.row_bytes(K, "base3")
+        assert bl.bitlinear_packed_row_bytes(K, "1bit") == oracle.row_bytes(K, "1bit")
     assert bl.bitlinear_packed_row_bytes(0, "2bit") == -1
     assert bl.bitlinear_packed_row_bytes(16, 7) == -1
     assert bl.bitlinear_packed_row_bytes(4096, "2bit") == 1024
     assert bl.bitlinear_packed_row_bytes(4096, "base3") == 832
+    assert bl.bitlinear_packed_row_bytes(4096, "1bit") == 512
     assert bl.bitlinear_pack_workspace_bytes(0, 5) == 0
     assert bl.bitlinear_pack_workspace_bytes(4096, 4096) % 16 == 0
 
@@ -84,6 +86,7 @@ def _fwd(bl, **kw):
     dict(gamma=P + 2),
     dict(packed=P + 8), dict(N=0), dict(N=-1), dict(K=0), dict(K=16909321), dict(dt=2),
     dict(scheme=5), dict(layout=3), dict(eps=-1.0), dict(eps=float("nan")), dict(wsb=0),
+    dict(layout=2, scheme=0),  # the 1-bit layout holds binary codes only
 ])
 def test_pack_rejects(bl, kw):
     assert _pack(bl, **kw) == bl.BL_ERR_INVALID_ARG
@@ -101,7 +104,7 @@ def test_quant_rejects(bl, kw):
     dict(xq=None), dict(scale=None), dict(packed=None), dict(gamma=None), dict(y=None),
     dict(gamma=P + 1),
     dict(y=P + 4), dict(acc=P + 4), dict(M=-1), dict(N=-1), dict(K=0), dict(K=16909321),
-    dict(layout=2), dict(ydt=3),
+    dict(layout=3), dict(ydt=3),
 ])
 def test_forward_rejects(bl, kw):
     assert _fwd(bl, **kw) == bl.BL_ERR_INVALID_ARG
@@ -151,6 +154,7 @@ def test_backward_rejects_and_limits(bl):
     assert bi(N=(1 << 24) + 8) == bl.BL_ERR_INVALID_ARG
     assert bi(dt=5) == bl.BL_ERR_INVALID_ARG
     assert bi(layout=4) == bl.BL_ERR_INVALID_ARG
+    assert bi(layout=2) == bl.BL_ERR_UNSUPPORTED  # grad_x reads 2-bit codes only
     assert bi(dt=0) == bl.BL_ERR_UNSUPPORTED       # fp32 grad_y
     assert bi(layout=1) == bl.BL_ERR_UNSUPPORTED   # base-3 codes
     assert bi(N=60) == bl.BL_ERR_UNSUPPORTED       # N % 8 != 0
@@ -211,5 +215,6 @@ def test_lut_rejects_and_limits(bl):
     assert f(K=0) == bl.BL_ERR_INVALID_ARG
     assert f(layout=5) == bl.BL_ERR_INVALID_ARG
     assert f(layout=0) == bl.BL_ERR_UNSUPPORTED
+    assert f(layout=2) == bl.BL_ERR_UNSUPPORTED
     assert f(M=2) == bl.BL_ERR_UNSUPPORTED
     assert f(M=0) == bl.BL_OK and f(N=0) == bl.BL_OK
