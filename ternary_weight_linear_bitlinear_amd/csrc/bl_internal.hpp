@@ -24,13 +24,22 @@ constexpr int kBF16 = 1;
 constexpr int64_t kSkinnyMaxM = 16;
 
 // Kernels using more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-// must raise their limit once. `done` is a flag owned by the caller, one per
-// kernel; setting the attribute twice is harmless, so a race is benign.
+// must raise their limit once, to what the kernel's static LDS leaves free
+// (asking for all 160 KiB fails when the kernel also has static arrays).
+// `done` is a flag owned by the caller, one per kernel; setting the attribute
+// twice is harmless, so a race is benign. A request above the free space is
+// refused here instead of failing at launch.
 template <typename F>
 hipError_t allow_dynamic_lds(F *kernel, size_t bytes, int *done) {
     if (bytes <= 65536 || *done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    constexpr size_t kLdsBytes = 160 * 1024;
+    hipFuncAttributes attr{};
+    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel));
+    if (e != hipSuccess) return e;
+    if (attr.sharedSizeBytes + bytes > kLdsBytes) return hipErrorInvalidValue;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(kLdsBytes - attr.sharedSizeBytes));
     if (e == hipSuccess) *done = 1;
     return e;
 }

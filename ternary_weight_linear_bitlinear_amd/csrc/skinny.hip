@@ -320,7 +320,7 @@ constexpr int kFusedMaxM = 4;
 constexpr int kFusedBlocksPerCu = 2;
 constexpr int kFsKS = 8, kFsNSS = 2;
 
-template <int LAYOUT, int KS, int NSS, int MAXM, bool STREAM, typename XT, typename YT>
+template <int LAYOUT, int KS, int NSS, int MAXM, bool STREAM, int RG, typename XT, typename YT>
 __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const XT *__restrict__ x, const uint8_t *__restrict__ packed,
     const GammaMap gm, int M, int64_t N, int64_t K, int64_t rb,
@@ -331,8 +331,10 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     constexpr int kRoundK = kRoundUnits * C::kUnitCodes;
     constexpr int kActStride = kRoundK + 16;
     // STREAM: the block streams tiles (see below); otherwise it owns one tile
-    // and keeps the register count that lets more blocks stay resident.
+    // and keeps the register count that lets more blocks stay resident. A
+    // tile is RG groups of 16 weight rows that share every activation read.
     constexpr bool kStream = STREAM;
+    static_assert(!STREAM || RG == 1, "streaming blocks take one row group per tile");
     // LDS: [base-3 table] [activation tile, MAXM rows] [two partial-sum areas]
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem);
@@ -345,25 +347,28 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     const int lane = threadIdx.x % 64;
     const int r = lane % 16;
     const int g = lane / 16;
-    const int64_t tiles = (N + 15) / 16;  // 16 weight rows per tile
+    const int64_t tiles = (N + 16 * RG - 1) / (16 * RG);
     const int64_t units = rb / C::kUnitBytes;
     const bool vec = (K % 8) == 0;
 
     float gs[kMaxSegments];
     load_gammas(gm, gs);
     // this lane's weight units of tile `tile`, round starting at unit u0
-    uint4 wv[NSS], wn[NSS];
-    bool wok[NSS], wnok[NSS];
-    auto issue = [&](int64_t tile, int64_t u0, uint4 (&w)[NSS], bool (&ok)[NSS]) {
-        const int64_t n = tile * 16 + r;
-        const uint8_t *wrow = packed + n * rb;
+    uint4 wv[RG][NSS], wn[RG][NSS];
+    bool wok[RG][NSS], wnok[RG][NSS];
+    auto issue = [&](int64_t tile, int64_t u0, uint4 (&w)[RG][NSS], bool (&ok)[RG][NSS]) {
 #pragma unroll
-        for (int s = 0; s < NSS; ++s) {
-            const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
-            ok[s] = n < N && unit < units;
-            // out-of-range lanes read a valid address; the value is zeroed
-            // where it is consumed, so no wait is forced here
-            w[s] = load_unit<LAYOUT>(ok[s] ? wrow + unit * C::kUnitBytes : packed);
+        for (int q = 0; q < RG; ++q) {
+            const int64_t n = (tile * RG + q) * 16 + r;
+            const uint8_t *wrow = packed + n * rb;
+#pragma unroll
+            for (int s = 0; s < NSS; ++s) {
+                const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
+                ok[q][s] = n < N && unit < units;
+                // out-of-range lanes read a valid address; the value is zeroed
+                // where it is consumed, so no wait is forced here
+                w[q][s] = load_unit<LAYOUT>(ok[q][s] ? wrow + unit * C::kUnitBytes : packed);
+            }
         }
     };
 
@@ -502,7 +507,9 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
 
     int buf = 0;
     for (int64_t tile = tile0; tile < tiles; tile += gridDim.x) {
-        v4i acc = {0, 0, 0, 0};
+        v4i acc[RG];
+#pragma unroll
+        for (int q = 0; q < RG; ++q) acc[q] = v4i{0, 0, 0, 0};
         for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
             if (!one_round) {
                 if (u0 > 0 || tile != tile0) {
@@ -521,8 +528,11 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
             }
 #pragma unroll
             for (int s = 0; s < NSS; ++s) {
-                int c[20];
-                decode_unit<LAYOUT>(wok[s] ? wv[s] : make_uint4(0u, 0u, 0u, 0u), lut, c);
+                int c[RG][20];
+#pragma unroll
+                for (int q = 0; q < RG; ++q)
+                    decode_unit<LAYOUT>(wok[q][s] ? wv[q][s] : make_uint4(0u, 0u, 0u, 0u), lut,
+                                        c[q]);
                 const int ul = (s * KS + wave) * 4 + g;
 #pragma unroll
                 for (int st = 0; st < C::kSteps; ++st) {
@@ -530,64 +540,72 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
                     if (r < M)
                         b = *reinterpret_cast<const v4i *>(act + r * kActStride +
                                                            ul * C::kUnitCodes + 16 * st);
-                    const v4i a = {c[4 * st], c[4 * st + 1], c[4 * st + 2], c[4 * st + 3]};
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < RG; ++q) {
+                        const v4i a = {c[q][4 * st], c[q][4 * st + 1], c[q][4 * st + 2],
+                                       c[q][4 * st + 3]};
+                        acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[q], 0, 0, 0);
+                    }
                 }
             }
         }
         if (kStream && one_round) {
             const int64_t ahead = tile + 2 * (int64_t)gridDim.x;
 #pragma unroll
-            for (int s = 0; s < NSS; ++s) {
-                wv[s] = wn[s];
-                wok[s] = wnok[s];
-            }
+            for (int q = 0; q < RG; ++q)
+#pragma unroll
+                for (int s = 0; s < NSS; ++s) {
+                    wv[q][s] = wn[q][s];
+                    wok[q][s] = wnok[q][s];
+                }
             if (ahead < tiles) issue(ahead, 0, wn, wnok);
         }
 
         // sum over the waves through LDS; two areas, so one barrier per tile
         // suffices (an area is rewritten only after the next tile's barrier,
-        // which wave 0 reaches after its reads of this one)
-        v4i *pb = part + buf * (KS * 64);
+        // which the reducing waves reach after their reads of this one)
+        v4i *pb = part + buf * (RG * KS * 64);
         buf ^= 1;
-        pb[wave * 64 + lane] = acc;
+#pragma unroll
+        for (int q = 0; q < RG; ++q) pb[(q * KS + wave) * 64 + lane] = acc[q];
         lds_barrier();
-        if (wave != 0 || r >= M) {
-            if constexpr (kStream) continue;
-            break;
-        }
-        v4i tot = pb[lane];
-#pragma unroll
-        for (int w = 1; w < KS; ++w) tot += pb[w * 64 + lane];
         const int t = r;
-        float fs[kMaxSegments];
-        seg_factors(gm, gs, tok_scale[t], fs);
-        const int64_t n0 = tile * 16;
+        if (t < M) {
+            float fs[kMaxSegments];
+            seg_factors(gm, gs, tok_scale[t], fs);
+            for (int q = wave; q < RG; q += KS) {  // wave q finishes row group q
+                v4i tot = pb[(q * KS) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t n = n0 + 4 * g + i;
-            if (n >= N) continue;
-            const int32_t a = tot[i];
-            const float v = (float)a * seg_pick(gm, fs, n);
-            if constexpr (sizeof(YT) == 4)
-                y[(int64_t)t * N + n] = v;
-            else
-                y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
-            if (acc_out) acc_out[(int64_t)t * N + n] = a;
+                for (int w = 1; w < KS; ++w) tot += pb[(q * KS + w) * 64 + lane];
+                const int64_t n0 = (tile * RG + q) * 16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t n = n0 + 4 * g + i;
+                    if (n >= N) continue;
+                    const int32_t a = tot[i];
+                    const float v = (float)a * seg_pick(gm, fs, n);
+                    if constexpr (sizeof(YT) == 4)
+                        y[(int64_t)t * N + n] = v;
+                    else
+                        y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
+                    if (acc_out) acc_out[(int64_t)t * N + n] = a;
+                }
+            }
         }
         if constexpr (!kStream) break;  // one tile per block
     }
 }
 
-template <int LAYOUT, int MAXM, int KS, int NSS, bool STREAM, typename XT, typename YT>
+template <int LAYOUT, int MAXM, int KS, int NSS, bool STREAM, typename XT, typename YT,
+          int RG = 1>
 hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, int64_t grid, YT *y, int32_t *acc,
                            hipStream_t s) {
     const int64_t rb = row_bytes_of(LAYOUT, K);
     constexpr int64_t kRoundK = (int64_t)KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes;
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (size_t)MAXM * (kRoundK + 16) +
-                        2 * (size_t)KS * 1024;
-    auto kern = linear_decode_kernel<LAYOUT, KS, NSS, MAXM, STREAM, XT, YT>;
+                        2 * (size_t)RG * KS * 1024;
+    auto kern = linear_decode_kernel<LAYOUT, KS, NSS, MAXM, STREAM, RG, XT, YT>;
     static int lds_raised = 0;
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
@@ -596,10 +614,11 @@ hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &g
     return hipGetLastError();
 }
 
-// One 16-row tile per block, except for several tokens whose rows fit one
-// round (K % 16 == 0) when the tiles outnumber kFusedBlocksPerCu blocks per
-// compute unit: quantising x in every block would then dominate, so the grid
-// is capped there and each block streams several tiles. A one-token
+// One tile per block (16 rows; 32 for one token from kWideN rows on), except
+// for several tokens whose rows fit one round (K % 16 == 0) when the tiles
+// outnumber kFusedBlocksPerCu blocks per compute unit: quantising x in every
+// block would then dominate, so the grid is capped there and each block
+// streams several tiles. A one-token
 // specialisation keeps only 16 values of x per thread, which leaves registers
 // for more resident blocks.
 template <int LAYOUT, typename XT, typename YT>
@@ -614,9 +633,12 @@ hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &g
                                                                           K, cap, y, acc, s);
     }
     if (N >= kWideN) {
+        // one token: two row groups per block halve the per-block work of
+        // reading and quantising x (32768 x 4096: 11.4 -> 10.8 us 2-bit,
+        // 11.3 -> 9.9 us 1-bit; four groups or eight waves were slower)
         if (M == 1)
-            return launch_linear_m<LAYOUT, 1, 4, 4, false>(x, packed, gamma, M, N, K, tiles, y,
-                                                           acc, s);
+            return launch_linear_m<LAYOUT, 1, 4, 4, false, XT, YT, 2>(x, packed, gamma, M, N, K,
+                                                                      (N + 31) / 32, y, acc, s);
         return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4, false>(x, packed, gamma, M, N, K, tiles,
                                                                 y, acc, s);
     }

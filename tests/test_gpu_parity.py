@@ -293,6 +293,9 @@ def test_zero_activation_row_gives_zero_output(bl):
                                          (3, 33, 17, "f32"), (4, 300, 4099, "bf16"),
                                          (1, 4096, 11008, "bf16"), (4, 64, 8192, "f32"),
                                          (1, 16400, 160, "bf16"), (3, 16384, 5000, "f32"),
+                                         # one token, two 16-row groups per block; the
+                                         # last block holds a single row
+                                         (1, 16385, 4096, "f32"),
                                          # several tokens, more 16-row tiles than the
                                          # capped grid (two blocks per compute unit):
                                          # blocks stream tiles; ragged last tile
