@@ -614,17 +614,29 @@ hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &g
     return hipGetLastError();
 }
 
-// One tile per block (16 rows; 32 for one token from kWideN rows on), except
-// for several tokens whose rows fit one round (K % 16 == 0) when the tiles
-// outnumber kFusedBlocksPerCu blocks per compute unit: quantising x in every
-// block would then dominate, so the grid is capped there and each block
-// streams several tiles. A one-token
+// Launch shapes, measured on MI355X. Below kWideN rows: one 16-row tile per
+// block, except for several tokens whose rows fit one round (K % 16 == 0)
+// when the tiles outnumber kFusedBlocksPerCu blocks per compute unit:
+// quantising x in every block would then dominate, so the grid is capped and
+// each block streams several tiles. From kWideN rows on: 4-wave blocks of two
+// row groups (four for several tokens from 2 kWideN rows on), which cut the
+// same per-block work while every weight load stays in flight. A one-token
 // specialisation keeps only 16 values of x per thread, which leaves registers
 // for more resident blocks.
 template <int LAYOUT, typename XT, typename YT>
 hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &gamma, int64_t M,
                            int64_t N, int64_t K, YT *y, int32_t *acc, hipStream_t s) {
     const int64_t tiles = (N + 15) / 16;
+    if (M > 1 && N >= kWideN) {
+        // several tokens, many rows: 2 (from 32768 rows on 4) row groups per
+        // block instead of a capped grid (M=2, 16384 rows: 10.7 -> 9.0 us;
+        // 32768 rows: 16.2 -> 14.3 us)
+        if (N >= 2 * kWideN)
+            return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4, false, XT, YT, 4>(
+                x, packed, gamma, M, N, K, (N + 63) / 64, y, acc, s);
+        return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4, false, XT, YT, 2>(
+            x, packed, gamma, M, N, K, (N + 31) / 32, y, acc, s);
+    }
     if (M > 1 && K % 16 == 0 &&
         K <= (int64_t)kFsKS * kFsNSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes) {
         const int64_t cap = (int64_t)kFusedBlocksPerCu * device_cu_count();
@@ -636,11 +648,8 @@ hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &g
         // one token: two row groups per block halve the per-block work of
         // reading and quantising x (32768 x 4096: 11.4 -> 10.8 us 2-bit,
         // 11.3 -> 9.9 us 1-bit; four groups or eight waves were slower)
-        if (M == 1)
-            return launch_linear_m<LAYOUT, 1, 4, 4, false, XT, YT, 2>(x, packed, gamma, M, N, K,
-                                                                      (N + 31) / 32, y, acc, s);
-        return launch_linear_m<LAYOUT, kFusedMaxM, 4, 4, false>(x, packed, gamma, M, N, K, tiles,
-                                                                y, acc, s);
+        return launch_linear_m<LAYOUT, 1, 4, 4, false, XT, YT, 2>(x, packed, gamma, M, N, K,
+                                                                  (N + 31) / 32, y, acc, s);
     }
     if (M == 1)
         return launch_linear_m<LAYOUT, 1, kFdKS, kFdNSS, false>(x, packed, gamma, M, N, K, tiles,

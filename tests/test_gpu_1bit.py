@@ -122,7 +122,7 @@ def test_prefill_1bit_full_size_sampled(bl):
 
 FUSED_CASES = [(1, 256, 256, "f32"), (2, 100, 1000, "bf16"), (3, 33, 17, "f32"),
                (4, 300, 9001, "bf16"), (1, 16400, 160, "bf16"), (3, 12000, 4096, "bf16"),
-               (4, 9000, 4096, "f32")]
+               (4, 9000, 4096, "f32"), (2, 20000, 512, "bf16"), (3, 33000, 300, "f32")]
 
 
 @pytest.mark.parametrize("M,N,K,dtype", FUSED_CASES)

@@ -296,6 +296,8 @@ def test_zero_activation_row_gives_zero_output(bl):
                                          # one token, two 16-row groups per block; the
                                          # last block holds a single row
                                          (1, 16385, 4096, "f32"),
+                                         # several tokens, four row groups per block
+                                         (2, 32800, 256, "bf16"), (4, 32769, 100, "f32"),
                                          # several tokens, more 16-row tiles than the
                                          # capped grid (two blocks per compute unit):
                                          # blocks stream tiles; ragged last tile

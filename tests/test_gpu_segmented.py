@@ -132,11 +132,14 @@ def test_linear_segmented_parity(bl, layout, M):
 
 
 @pytest.mark.parametrize("layout", ["2bit", "base3"])
-def test_linear_segmented_streaming(bl, layout):
-    """Fused decode of 3 tokens over a stack with more 16-row tiles than the
-    capped grid, so blocks stream tiles across segment boundaries (ragged
-    segments, the last tile partly empty)."""
-    segs, K = (4100, 1030, 3000), 1024
+@pytest.mark.parametrize("segs", [(4100, 1030, 3500), (8000, 4000, 4500), (20000, 9000, 4000)])
+def test_linear_segmented_streaming(bl, layout, segs):
+    """Fused decode of 3 tokens over stacks whose segment boundaries fall
+    inside blocks: 8630 rows (540 tiles, more than the capped grid of two
+    blocks per compute unit: blocks stream tiles), 16500 rows (two 16-row
+    groups per block), 33000 rows (four); ragged segments, the last tile
+    partly empty."""
+    K = 1024
     M = 3
     banner(f"linear_segmented streaming {layout} M={M} segs={segs} K={K}")
     codes, gammas, packed = stacked(segs, K, layout, seed=77)
