@@ -159,8 +159,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // an out-of-range chunk reads a valid address and is zeroed by a select,
     // so no control flow splits the load stream and the compiler can keep all
     // of a tile's loads in flight. Other row lengths take a byte-wise path.
-    // Interior tiles (whole tile inside M and N, and an even number of full
-    // k-tiles) load without guards: the k-tile index is clamped so that the
+    // Interior tiles (whole tile inside M and N, an even number of full
+    // k-tiles and no padding codes) load without guards: the k-tile index is clamped so that the
     // prefetches past the last tile re-read a valid tile whose data is never
     // used. Edge tiles zero out-of-range chunks: they read a valid address and
     // select zero, so no branch splits the load stream. Rows that are not a
@@ -320,7 +320,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         }
 
     };
-    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 4) == 0;
+    // interior also needs rows without padding codes (K = every code the
+    // units hold): unguarded activation loads past K would read the next row
+    // (or past the end of xq) and meet padding codes, which are -1, not 0, in
+    // the 1-bit layout
+    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 4) == 0 &&
+                          K == units * C::UC;
     if (interior)
         run(std::integral_constant<bool, false>{});
     else

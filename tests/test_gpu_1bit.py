@@ -81,6 +81,9 @@ FWD_CASES = [
     (1, 256, 256), (3, 100, 1000), (5, 33, 17), (16, 300, 4099), (16, 8200, 64),
     # tiled GEMM: edge tiles, ragged K, several k-tiles
     (17, 64, 130), (300, 520, 264), (40, 1000, 333), (257, 700, 5000),
+    # whole tiles over rows with padding codes (K = 976 in 1024-code rows): the
+    # unguarded interior path must not run there (regression)
+    (183, 478, 976), (256, 128, 976),
 ]
 
 

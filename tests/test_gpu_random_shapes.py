@@ -1,0 +1,78 @@
+"""Seeded random shapes through every product path, against the oracle.
+
+Each case draws a layout (2-bit, base-3, 1-bit with binary codes), input and
+output dtypes, and M, N, K with ragged edges: M <= 4 runs the fused decode
+step, 5 <= M <= 16 the decode product, larger M the tiled GEMM (both after
+the stand-alone quantiser). Accumulators must match the oracle bit for bit
+(outside elements on a rounding boundary, which are excluded and bounded as
+in the other parity tests), outputs within the output tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_linear_bitlinear_amd import synth
+from parity_util import (check_codes, check_y_bf16, check_y_f32, excluded_acc_mask, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from ternary_weight_linear_bitlinear_amd import bitlinear
+    return bitlinear
+
+
+def dev(a: np.ndarray, bf16: bool) -> torch.Tensor:
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def draw_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        layout = ["2bit", "base3", "1bit"][i % 3]
+        band = i % 4  # fused, decode product, GEMM, GEMM with many rows
+        M = [int(rng.integers(1, 5)), int(rng.integers(5, 17)), int(rng.integers(17, 130)),
+             int(rng.integers(130, 400))][band]
+        N = int(rng.integers(1, 700))
+        K = int(rng.integers(1, 1300))
+        cases.append((i, layout, M, N, K, ["f32", "bf16"][int(rng.integers(0, 2))],
+                      [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_cases(48, 2024), ids=lambda c: f"{c[1]}-M{c[2]}-N{c[3]}-K{c[4]}")
+def test_random_shape_parity(bl, case):
+    i, layout, M, N, K, dtype, out_dtype = case
+    print(f"[case] random {i}: {layout} M={M} N={N} K={K} {dtype} -> {out_dtype}", flush=True)
+    scheme = "binary" if layout == "1bit" else "ternary"
+    p = synth.make_problem(M=M, N=N, K=K, seed=5000 + i, dtype=dtype, outlier_frac=0.01)
+    bf = dtype == "bf16"
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, bf), layout, scheme)
+    x = dev(p.x_store, bf)
+    ref = oracle.forward(p.w, p.x, layout, scheme)
+    codes_gpu, bad = oracle.unpack(to_np(packed), K, layout)
+    assert bad == 0
+    check_codes(codes_gpu, ref["codes"], ref["wflags"], "codes")
+    if M <= 4:
+        y, acc = bl.bitlinear_linear(x, packed, gamma, N, layout, out_dtype, acc=True)
+        xq_bad = np.zeros_like(ref["xq"], bool)  # same fp32 steps as the oracle
+    else:
+        xq, scale = bl.bitlinear_quant_acts(x)
+        y, acc = bl.bitlinear_forward(xq, scale, packed, gamma, N, K, layout, out_dtype,
+                                      acc=True)
+        torch.cuda.synchronize()
+        check_codes(to_np(xq), ref["xq"], ref["xflags"], "xq")
+        assert np.array_equal(to_np(scale), ref["scale"])
+        xq_bad = to_np(xq) != ref["xq"]
+    torch.cuda.synchronize()
+    ex = excluded_acc_mask(xq_bad, codes_gpu != ref["codes"])
+    assert np.array_equal(to_np(acc)[~ex], ref["acc"][~ex])
+    if out_dtype == torch.float32:
+        check_y_f32(to_np(y)[~ex], ref["y64"][~ex])
+    else:
+        check_y_bf16(to_np(y.view(torch.int16)).view(np.uint16)[~ex], ref["y64"][~ex])
