@@ -35,17 +35,18 @@ def draw_cases(n, seed):
     cases = []
     for i in range(n):
         layout = ["2bit", "base3", "1bit"][i % 3]
-        band = i % 4  # fused, decode product, GEMM, GEMM with many rows
+        band = i % 5  # fused, decode product, GEMM, GEMM with many rows, fused many rows
         M = [int(rng.integers(1, 5)), int(rng.integers(5, 17)), int(rng.integers(17, 130)),
-             int(rng.integers(130, 400))][band]
-        N = int(rng.integers(1, 700))
-        K = int(rng.integers(1, 1300))
+             int(rng.integers(130, 400)), int(rng.integers(1, 5))][band]
+        # many rows: the capped streaming grid and the two- and four-group blocks
+        N = int(rng.integers(8000, 40000)) if band == 4 else int(rng.integers(1, 700))
+        K = int(rng.integers(16, 700)) // 16 * 16 if band == 4 else int(rng.integers(1, 1300))
         cases.append((i, layout, M, N, K, ["f32", "bf16"][int(rng.integers(0, 2))],
                       [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]))
     return cases
 
 
-@pytest.mark.parametrize("case", draw_cases(48, 2024), ids=lambda c: f"{c[1]}-M{c[2]}-N{c[3]}-K{c[4]}")
+@pytest.mark.parametrize("case", draw_cases(60, 2024), ids=lambda c: f"{c[1]}-M{c[2]}-N{c[3]}-K{c[4]}")
 def test_random_shape_parity(bl, case):
     i, layout, M, N, K, dtype, out_dtype = case
     print(f"[case] random {i}: {layout} M={M} N={N} K={K} {dtype} -> {out_dtype}", flush=True)
@@ -76,3 +77,53 @@ def test_random_shape_parity(bl, case):
         check_y_f32(to_np(y)[~ex], ref["y64"][~ex])
     else:
         check_y_bf16(to_np(y.view(torch.int16)).view(np.uint16)[~ex], ref["y64"][~ex])
+
+
+def draw_stacks(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        layout = ["2bit", "base3", "1bit"][i % 3]
+        nseg = int(rng.integers(1, 9))
+        big = i % 2 == 1
+        segs = tuple(int(v) for v in rng.integers(1, 6000 if big else 300, size=nseg))
+        M = int(rng.integers(1, 5)) if i % 4 < 2 else int(rng.integers(5, 200))
+        K = int(rng.integers(1, 600))
+        out.append((i, layout, M, segs, K))
+    return out
+
+
+@pytest.mark.parametrize("case", draw_stacks(24, 77),
+                         ids=lambda c: f"{c[1]}-M{c[2]}-segs{len(c[3])}-K{c[4]}")
+def test_random_stack_parity(bl, case):
+    """Random stacks of 1..8 row segments, each with its own scale, through the
+    segmented calls: the fused step for M <= 4 (from bf16 x), quantise + the
+    segmented product otherwise. Every segment must equal the oracle on it."""
+    i, layout, M, segs, K = case
+    print(f"[case] random stack {i}: {layout} M={M} segs={segs} K={K}", flush=True)
+    rng = np.random.default_rng(9000 + i)
+    if layout == "1bit":  # binary codes only
+        codes = [np.where(rng.random((n, K)) < 0.5, -1, 1).astype(np.int8) for n in segs]
+    else:
+        codes = [rng.integers(-1, 2, size=(n, K)).astype(np.int8) for n in segs]
+    scales = np.zeros(max(4, (len(segs) + 3) // 4 * 4), np.float32)
+    scales[:len(segs)] = rng.uniform(0.005, 0.05, size=len(segs))
+    packed = dev(np.concatenate([oracle.pack(c, layout) for c in codes], axis=0), False)
+    p = synth.make_problem(M=M, N=1, K=K, seed=9500 + i, dtype="bf16", outlier_frac=0.01)
+    x = dev(p.x_store, True)
+    if M <= 4:
+        y, acc = bl.bitlinear_linear_segmented(x, packed, dev(scales, False), segs, layout,
+                                               acc=True)
+    else:
+        xq, scale = bl.bitlinear_quant_acts(x)
+        y, acc = bl.bitlinear_forward_segmented(xq, scale, packed, dev(scales, False), segs, K,
+                                                layout, acc=True)
+    torch.cuda.synchronize()
+    xq_ref, s_ref, _ = oracle.quant_acts(p.x)  # same fp32 steps on both sides
+    acc_ref = oracle.int_product(xq_ref, np.concatenate(codes, axis=0))
+    assert np.array_equal(to_np(acc), acc_ref)
+    cols, parts = 0, []
+    for c, g in zip(codes, scales):
+        parts.append(oracle.epilogue(acc_ref[:, cols:cols + c.shape[0]], g, s_ref))
+        cols += c.shape[0]
+    check_y_f32(to_np(y), np.concatenate(parts, axis=1))
