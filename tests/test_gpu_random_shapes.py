@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from ternary_weight_linear_bitlinear_amd import synth
-from parity_util import (check_codes, check_y_bf16, check_y_f32, excluded_acc_mask, to_np)
+from parity_util import (SCALE_RTOL, check_codes, check_rel, check_y_bf16, check_y_f32,
+                         excluded_acc_mask, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +128,70 @@ def test_random_stack_parity(bl, case):
         parts.append(oracle.epilogue(acc_ref[:, cols:cols + c.shape[0]], g, s_ref))
         cols += c.shape[0]
     check_y_f32(to_np(y), np.concatenate(parts, axis=1))
+
+
+def draw_packs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        layout = ["2bit", "base3", "1bit"][i % 3]
+        scheme = "binary" if layout == "1bit" else ["ternary", "binary"][int(rng.integers(0, 2))]
+        out.append((i, layout, scheme, int(rng.integers(1, 400)), int(rng.integers(1, 3000)),
+                    ["f32", "bf16"][int(rng.integers(0, 2))]))
+    return out
+
+
+@pytest.mark.parametrize("case", draw_packs(24, 31),
+                         ids=lambda c: f"{c[1]}-{c[2]}-N{c[3]}-K{c[4]}-{c[5]}")
+def test_random_pack_parity(bl, case):
+    """Random shapes through the packer: the weight scale, every code (outside
+    boundary flags) and every packed byte, padding included, against the
+    oracle's layout."""
+    i, layout, scheme, N, K, dtype = case
+    print(f"[case] random pack {i}: {layout} {scheme} N={N} K={K} {dtype}", flush=True)
+    p = synth.make_problem(M=1, N=N, K=K, seed=7000 + i, dtype=dtype)
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, dtype == "bf16"), layout, scheme)
+    torch.cuda.synchronize()
+    if scheme == "ternary":
+        codes, flags, g_ref = oracle.ternary_codes(p.w)
+    else:
+        codes, flags, _alpha, g_ref = oracle.binary_codes(p.w)
+    g = to_np(gamma)[0]
+    check_rel([g], [g_ref], SCALE_RTOL, "weight scale")
+    got = to_np(packed)
+    codes_gpu, bad = oracle.unpack(got, K, layout)
+    assert bad == 0
+    assert check_codes(codes_gpu, codes, flags, "codes") == 0 or g != g_ref
+    assert np.array_equal(oracle.pack(codes_gpu, layout), got)
+
+
+def draw_bwd(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 300)), int(rng.integers(1, 80)) * 8,
+             int(rng.integers(1, 100)) * 8) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", draw_bwd(12, 5), ids=lambda c: f"M{c[1]}-N{c[2]}-K{c[3]}")
+def test_random_backward_parity(bl, case):
+    """Random shapes through both straight-through-estimator products, to the
+    fp32 summation bound of the backward tests (n u sum|terms| + u |ref|)."""
+    i, M, N, K = case
+    print(f"[case] random backward {i}: M={M} N={N} K={K}", flush=True)
+    u = 2.0 ** -24
+    p = synth.make_problem(M=M, N=N, K=K, seed=8000 + i, dtype="bf16", grad_std=1e-3)
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, True), "2bit")
+    gy = dev(p.grad_y_store, True)
+    gx = bl.bitlinear_backward_input(gy, packed, gamma, K)
+    gw = bl.bitlinear_backward_weight(gy, dev(p.x_store, True))
+    torch.cuda.synchronize()
+    codes, bad = oracle.unpack(to_np(packed), K, "2bit")
+    assert bad == 0
+    g = float(to_np(gamma)[0])
+    ref = oracle.ste_grad_x(p.grad_y, codes, g)
+    s = (np.abs(p.grad_y.astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
+    err = np.abs(to_np(gx).astype(np.float64) - ref)
+    assert np.all(err <= 1.01 * (N * u * s + u * np.abs(ref)) + 1e-30), "grad_x"
+    ref = oracle.ste_grad_w(p.grad_y, p.x)
+    s = np.abs(p.grad_y.astype(np.float64)).T @ np.abs(p.x.astype(np.float64))
+    err = np.abs(to_np(gw).astype(np.float64) - ref)
+    assert np.all(err <= 1.01 * (M * u * s + u * np.abs(ref)) + 1e-30), "grad_w"
