@@ -160,7 +160,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // so no control flow splits the load stream and the compiler can keep all
     // of a tile's loads in flight. Other row lengths take a byte-wise path.
     // Interior tiles (whole tile inside M and N, an even number of full
-    // k-tiles and no padding codes) load without guards: the k-tile index is clamped so that the
+    // k-tiles; see below for rows with padding codes) load without guards: the k-tile index is clamped so that the
     // prefetches past the last tile re-read a valid tile whose data is never
     // used. Edge tiles zero out-of-range chunks: they read a valid address and
     // select zero, so no branch splits the load stream. Rows that are not a
@@ -175,7 +175,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             const int64_t m = m0 + row, k = kc0 + col * 16;
             if (!G) {
-                a_reg[i] = *reinterpret_cast<const v4i *>(xq + m * K + k);
+                // (a chunk is wholly below or above K: K % 16 == 0 here)
+                a_reg[i] = *reinterpret_cast<const v4i *>(xq + m * K + (k < K ? k : 0));
             } else if (EVEN_K) {
                 const bool ok = m < M && k < K;
                 const v4i v = *reinterpret_cast<const v4i *>(xq + (ok ? m * K + k : 0));
@@ -320,12 +321,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         }
 
     };
-    // interior also needs rows without padding codes (K = every code the
-    // units hold): unguarded activation loads past K would read the next row
-    // (or past the end of xq) and meet padding codes, which are -1, not 0, in
-    // the 1-bit layout
+    // Rows padded to whole units hold codes past K. Unguarded activation
+    // chunks past K read the row's first chunk instead (in bounds), whose
+    // values meet padding codes: 0 in the 2-bit and base-3 layouts, but -1 in
+    // the 1-bit layout, so there only rows without padding run unguarded.
     const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 4) == 0 &&
-                          K == units * C::UC;
+                          (LAYOUT != kLayout1Bit || K == units * C::UC);
     if (interior)
         run(std::integral_constant<bool, false>{});
     else
