@@ -136,7 +136,10 @@ bl_status bitlinear_quant_acts(const void *x, int x_dtype, int64_t M, int64_t K,
  *   y          out: [M, N], y_dtype BL_F32 or BL_BF16 (round to nearest even).
  *   acc        optional out: [M, N] int32 accumulators, or NULL.
  * Dispatch on M: small batches (M <= 16) stream the packed weights once;
- * larger M runs the tiled INT8 matrix-core product. */
+ * medium batches stream them once per 16-token chunk (all chunks in one
+ * launch) while that is measured faster, i.e. for a few chunks and moderate
+ * N; larger M runs the tiled INT8 matrix-core product. Results do not depend
+ * on the path (the INT32 sums are exact). */
 bl_status bitlinear_forward(const int8_t *xq, const float *scale,
                             const uint8_t *packed, int layout, const float *gamma,
                             int64_t M, int64_t N, int64_t K,

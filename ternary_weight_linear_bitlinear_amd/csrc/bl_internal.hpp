@@ -20,7 +20,8 @@ constexpr int kSchemeBinary = 1;
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
-// Largest batch handled by the weight-streaming (decode) kernel.
+// Tokens per launch-row of the weight-streaming (decode) kernel; larger
+// batches run as several such chunks in one launch (see skinny_handles).
 constexpr int64_t kSkinnyMaxM = 16;
 
 // Kernels using more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
@@ -103,6 +104,9 @@ hipError_t launch_quant_acts(const void *x, int dtype, int64_t M, int64_t K,
                              int8_t *xq, float *scale, hipStream_t stream);
 
 // ---- products (skinny.hip, gemm.hip) -------------------------------------
+// Whether the weight-streaming kernel (in 16-token chunks) or the tiled GEMM
+// takes an M x N product in `layout`.
+bool skinny_handles(int64_t M, int64_t N, int layout);
 hipError_t launch_forward_skinny(const int8_t *xq, const float *scale,
                                  const uint8_t *packed, int layout,
                                  const GammaMap &gamma, int64_t M, int64_t N,

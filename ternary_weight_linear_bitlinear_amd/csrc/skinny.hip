@@ -137,6 +137,15 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int r = lane % 16;  // weight row within a row group (A) / token (B)
     const int g = lane / 16;  // lane group = unit within the super-step
     const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
+    // larger batches run as chunks of MAXM tokens, one per grid row
+    {
+        const int64_t t0 = (int64_t)blockIdx.y * MAXM;
+        xq += t0 * K;
+        scale += t0;
+        y += t0 * N;
+        if (acc_out) acc_out += t0 * N;
+        M = M - (int)t0 < MAXM ? M - (int)t0 : MAXM;
+    }
     float gs[kMaxSegments];
     load_gammas(gm, gs);
 
@@ -272,10 +281,12 @@ hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *
                            int32_t *acc, hipStream_t s) {
     const int64_t rb = row_bytes_of(LAYOUT, K);
     // the partial-tile buffer aliases the activation area (needs KS*RG KiB)
-    const size_t act = (size_t)M * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
+    const int64_t chunk_m = M < MAXM ? M : MAXM;
+    const size_t act = (size_t)chunk_m * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
     const size_t part = (size_t)KS * RG * 1024;
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (act > part ? act : part);
-    dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG))), block(64 * KS);
+    dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)), (unsigned)((M + MAXM - 1) / MAXM)),
+        block(64 * KS);
     auto kern = skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, YT>;
     static int lds_raised = 0;  // one flag per instantiation of this launcher
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
@@ -708,6 +719,20 @@ hipError_t launch_forward_skinny(const int8_t *xq, const float *scale, const uin
 }
 
 int64_t fused_decode_max_m() { return kFusedMaxM; }
+
+// Batches above 16 tokens stream the weights once per 16-token chunk (all
+// chunks in one launch). That beats the tiled GEMM while the chunks times the
+// rows stay small: with few token tiles the GEMM keeps only N/64 blocks busy,
+// each walking all of K. Crossovers measured on MI355X (K = 4096 and 11008):
+// 2-bit and 1-bit up to 6 chunks at 4096 rows, 4 at 11008-12288 rows and 2 at
+// 32768 rows; base-3, whose decode costs more per byte, up to 4 chunks at
+// 4096 rows, 2 at 11008-12288 and none at 32768.
+bool skinny_handles(int64_t M, int64_t N, int layout) {
+    if (M <= kSkinnyMaxM) return true;
+    const int64_t chunks = (M + kSkinnyMaxM - 1) / kSkinnyMaxM;
+    if (layout == kLayoutBase3) return (chunks <= 2 && N <= 16384) || chunks * N <= 16384;
+    return chunks <= 2 || (chunks <= 6 && chunks * N <= 49152);
+}
 
 hipError_t launch_linear_decode(const void *x, int x_dtype, const uint8_t *packed, int layout,
                                 const GammaMap &gamma, int64_t M, int64_t N, int64_t K, void *y,
