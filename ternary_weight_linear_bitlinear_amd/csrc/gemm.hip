@@ -155,16 +155,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     v4i a_regs[DIST][C::ACH];
     uint4 b_regs[DIST][C::FJ];
 
-    // Loads are branch-free in the common case (rows a multiple of 16 bytes):
-    // an out-of-range chunk reads a valid address and is zeroed by a select,
-    // so no control flow splits the load stream and the compiler can keep all
-    // of a tile's loads in flight. Other row lengths take a byte-wise path.
-    // Interior tiles (whole tile inside M and N, an even number of full
-    // k-tiles; see below for rows with padding codes) load without guards: the k-tile index is clamped so that the
-    // prefetches past the last tile re-read a valid tile whose data is never
-    // used. Edge tiles zero out-of-range chunks: they read a valid address and
-    // select zero, so no branch splits the load stream. Rows that are not a
-    // multiple of 16 bytes take a byte-wise path.
+    // Interior tiles (the whole tile inside M and N, an even number of full
+    // k-tiles; rows with padding codes are discussed where `interior` is set)
+    // load without guards: the k-tile index is clamped, so the prefetches past
+    // the last tile re-read a valid tile whose data is never used. Edge tiles
+    // zero out-of-range chunks: they read a valid address and select zero, so
+    // no branch splits the load stream and the compiler can keep all of a
+    // tile's loads in flight. Rows that are not a multiple of 16 bytes take a
+    // byte-wise path.
     auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 *b_reg, auto guard_c) {
         constexpr bool G = decltype(guard_c)::value;
         if (!G) kt = kt < ktiles ? kt : ktiles - 1;

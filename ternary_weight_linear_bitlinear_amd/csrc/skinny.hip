@@ -344,7 +344,6 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     // STREAM: the block streams tiles (see below); otherwise it owns one tile
     // and keeps the register count that lets more blocks stay resident. A
     // tile is RG groups of 16 weight rows that share every activation read.
-    constexpr bool kStream = STREAM;
     static_assert(!STREAM || RG == 1, "streaming blocks take one row group per tile");
     // LDS: [base-3 table] [activation tile, MAXM rows] [two partial-sum areas]
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -417,7 +416,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
     // streaming (rows that fit one round): x is quantised once per block and
     // the block takes tiles tile0, tile0 + gridDim.x, ...; the next tile's
     // weights are always in flight while the current one is multiplied
-    if (kStream && one_round && tile0 + gridDim.x < tiles) issue(tile0 + gridDim.x, 0, wn, wnok);
+    if (STREAM && one_round && tile0 + gridDim.x < tiles) issue(tile0 + gridDim.x, 0, wn, wnok);
 
     if (LAYOUT == kLayoutBase3) {
         for (int i = threadIdx.x; i < 4 * 256; i += kThreads)
@@ -560,7 +559,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
                 }
             }
         }
-        if (kStream && one_round) {
+        if (STREAM && one_round) {
             const int64_t ahead = tile + 2 * (int64_t)gridDim.x;
 #pragma unroll
             for (int q = 0; q < RG; ++q)
@@ -603,7 +602,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
                 }
             }
         }
-        if constexpr (!kStream) break;  // one tile per block
+        if constexpr (!STREAM) break;  // one tile per block
     }
 }
 
