@@ -31,22 +31,28 @@ namespace {
 
 constexpr int kXcds = 8;
 
-template <int LAYOUT, int BM_, int BN_, int WM_, int WN_, int DIST_>
+template <int LAYOUT, int BM_, int BN_, int WM_, int WN_, int DIST_, int KG_ = 1>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int DIST = DIST_;  // k-tiles the global loads run ahead (1 or 2)
-    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int DIST = DIST_;  // k-tiles the global loads run ahead (1, 2 or 4)
+    static constexpr int KG = KG_;      // k-groups: wave groups splitting the k-tiles
+    static constexpr int kGroupThreads = 64 * WM * WN;
+    static constexpr int kThreads = kGroupThreads * KG;
     static constexpr int UC = LAYOUT == kLayoutBase3 ? 80 : 64;  // codes per unit
     static constexpr int LB = LAYOUT == kLayout1Bit ? 8 : 16;     // bytes per unit
     static constexpr int BK = 2 * UC;                             // codes per k-tile
     static constexpr int LDSK = BK + 16;                          // padded LDS row (bytes)
     static constexpr int KSTEPS = UC / 16;                        // MFMA k-steps per tile
-    static constexpr int ACH = BM * BK / 16 / kThreads;           // A 16B chunks per thread
+    static constexpr int ACH = BM * BK / 16 / kGroupThreads;      // A 16B chunks per thread
     static constexpr int FI = BM / WM / 32, FJ = BN / WN / 32;    // fragments per wave
     static constexpr int STAGE = BM * LDSK;
     static constexpr int LUT = LAYOUT == kLayoutBase3 ? 8192 : 0;
-    static constexpr int SMEM = LUT + 2 * STAGE;
-    static_assert(BM * BK % (16 * kThreads) == 0, "A tile must split evenly");
+    // each k-group stages its own tiles; afterwards groups 1..KG-1 hand their
+    // INT32 tile to group 0 through the same memory
+    static constexpr int STAGES = KG * 2 * STAGE, RED = (KG - 1) * BM * BN * 4;
+    static constexpr int SMEM = LUT + (STAGES > RED ? STAGES : RED);
+    static_assert(BM * BK % (16 * kGroupThreads) == 0, "A tile must split evenly");
+    static_assert(DIST == 1 || DIST == 2 || DIST == 4, "register sets: 1, 2 or 4");
 };
 
 // Expand one packed 16-byte unit into UC code bytes (natural order).
@@ -110,13 +116,14 @@ __device__ __forceinline__ int xcd_tile(int b, int ntiles) {
     return t < ntiles ? t : -1;
 }
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, bool EVEN_K, typename YT>
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG, bool EVEN_K,
+          typename YT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
-    using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
+    using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST, KG>;
     constexpr int kThreads = C::kThreads;
+    constexpr int kGT = C::kGroupThreads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem);
-    int8_t *stage0 = reinterpret_cast<int8_t *>(smem + C::LUT);
     const int8_t *__restrict__ xq = g.xq;
     const float *__restrict__ scale = g.scale;
     const uint8_t *__restrict__ packed = g.packed;
@@ -130,8 +137,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     const int64_t n0 = (int64_t)(t % tiles_n) * BN;
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64, lane = tid % 64;
+    // k-group kg (a run of whole waves, so kg is wave-uniform) and the
+    // thread's place within its group
+    const int kg = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / kGT);
+    const int gtid = KG == 1 ? tid : tid % kGT;
+    const int wave = gtid / 64, lane = tid % 64;
     const int wm = wave / WN, wn = wave % WN;
+    int8_t *stage0 = reinterpret_cast<int8_t *>(smem + C::LUT) + kg * 2 * C::STAGE;
     const int frow = lane % 32;  // fragment row (A) / column (B)
     const int lg = lane / 32;    // lane group: packed unit within the k-tile
 
@@ -155,8 +167,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     v4i a_regs[DIST][C::ACH];
     uint4 b_regs[DIST][C::FJ];
 
-    // Interior tiles (the whole tile inside M and N, an even number of full
-    // k-tiles; rows with padding codes are discussed where `interior` is set)
+    // Interior tiles (the whole tile inside M and N, full k-tiles; the exact
+    // conditions are stated where `interior` is set)
     // load without guards: the k-tile index is clamped, so the prefetches past
     // the last tile re-read a valid tile whose data is never used. Edge tiles
     // zero out-of-range chunks: they read a valid address and select zero, so
@@ -169,7 +181,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         const int64_t kc0 = kt * C::BK;
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
-            const int q = tid + i * kThreads;
+            const int q = gtid + i * kGT;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             const int64_t m = m0 + row, k = kc0 + col * 16;
             if (!G) {
@@ -207,7 +219,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     auto store_a = [&](int8_t *As, const v4i *a_reg) {
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
-            const int q = tid + i * kThreads;
+            const int q = gtid + i * kGT;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             *reinterpret_cast<v4i *>(As + row * C::LDSK + col * 16) = a_reg[i];
         }
@@ -221,12 +233,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // The loop body is free of branches: the k-tile count is rounded up to
-    // even, and loads of tiles past the end read valid addresses and are
-    // zeroed by the guards in load_tile, so those tiles add nothing. The loop
-    // is unrolled by two so that LDS buffers and register sets are static and
-    // the compiler can wait for exactly the loads a step consumes.
-    const int64_t kt_end = (ktiles + 1) & ~(int64_t)1;
+    // The loop is unrolled by U steps so that LDS buffers and register sets
+    // are static and the compiler can wait for exactly the loads a step
+    // consumes. With one group and two register sets the body is free of
+    // branches: the k-tile count is rounded up to even, and loads of tiles
+    // past the end read valid addresses and are zeroed by the guards in
+    // load_tile, so those tiles add nothing.
+    //
+    // With k-groups, group kg takes the k-tiles [k_lo, k_hi) of an equal
+    // share. Every group runs the same number of steps, so the barriers
+    // match; steps past a group's share (and, with four register sets, past
+    // the end) skip the multiply, a wave-uniform branch, and their loads read
+    // valid addresses.
+    constexpr int U = DIST > 2 ? DIST : 2;
+    constexpr bool kSkip = KG > 1 || DIST > 2;
+    int64_t k_lo = 0, k_hi = ktiles, kt_end = (ktiles + 1) & ~(int64_t)1;
+    if constexpr (kSkip) {
+        const int64_t share = (ktiles + KG - 1) / KG;
+        k_lo = kg * share;
+        k_hi = k_lo + share < ktiles ? k_lo + share : ktiles;
+        kt_end = k_lo + (share + U - 1) / U * U;
+    }
 
     // Multiply the k-tile in LDS buffer As by the weight units bu (one per
     // fragment column block). 2-bit: k-step ks consumes exactly word ks of a
@@ -276,30 +303,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     };
 
     auto run = [&](auto guard_c) {
-        if constexpr (DIST == 2) {
-            // LDS holds tiles kt and kt+1; registers hold kt+1 (arrived) and kt+2
-            // (in flight). S names the register set and LDS buffer of tile kt.
-            load_tile(0, a_regs[0], b_regs[0], guard_c);
-            load_tile(1, a_regs[DIST - 1], b_regs[DIST - 1], guard_c);
+        if constexpr (DIST >= 2) {
+            // LDS holds tiles kt and kt+1; registers hold kt+1 (arrived) up to
+            // kt+DIST (in flight). Register set S = (kt - k_lo) % DIST holds
+            // tile kt, LDS buffer S % 2.
+#pragma unroll
+            for (int d = 0; d < DIST; ++d) load_tile(k_lo + d, a_regs[d], b_regs[d], guard_c);
             store_a(stage0, a_regs[0]);
-            __syncthreads();  // tile 0 (and the decode table) ready
+            __syncthreads();  // tile k_lo (and the decode table) ready
             auto step = [&](int64_t kt, auto set_c) {
                 constexpr int S = decltype(set_c)::value;
+                constexpr int L = S % 2;
                 uint4 bu[C::FJ];
     #pragma unroll
                 for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[S][j];
-                load_tile(kt + 2, a_regs[S], b_regs[S], guard_c);
-                mma(stage0 + S * C::STAGE, bu);
-                store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[S ^ 1]);
+                load_tile(kt + DIST, a_regs[S], b_regs[S], guard_c);
+                if (!kSkip || kt < k_hi) mma(stage0 + L * C::STAGE, bu);
+                store_a(stage0 + (L ^ 1) * C::STAGE, a_regs[(S + 1) % DIST]);
                 lds_barrier();
             };
-            for (int64_t kt = 0; kt < kt_end; kt += 2) {
+            for (int64_t kt = k_lo; kt < kt_end; kt += U) {
                 step(kt, std::integral_constant<int, 0>{});
-                step(kt + 1, std::integral_constant<int, DIST - 1>{});
+                step(kt + 1, std::integral_constant<int, 1 % DIST>{});
+                if constexpr (U == 4) {
+                    step(kt + 2, std::integral_constant<int, 2 % DIST>{});
+                    step(kt + 3, std::integral_constant<int, 3 % DIST>{});
+                }
             }
         } else {
             // LDS holds tiles kt and kt+1; one register set carries tile kt+1.
-            load_tile(0, a_regs[0], b_regs[0], guard_c);
+            load_tile(k_lo, a_regs[0], b_regs[0], guard_c);
             store_a(stage0, a_regs[0]);
             __syncthreads();
             auto step = [&](int64_t kt, auto buf_c) {
@@ -308,11 +341,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     #pragma unroll
                 for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[0][j];
                 load_tile(kt + 1, a_regs[0], b_regs[0], guard_c);
-                mma(stage0 + S * C::STAGE, bu);
+                if (!kSkip || kt < k_hi) mma(stage0 + S * C::STAGE, bu);
                 store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0]);
                 lds_barrier();
             };
-            for (int64_t kt = 0; kt < kt_end; kt += 2) {
+            for (int64_t kt = k_lo; kt < kt_end; kt += 2) {
                 step(kt, std::integral_constant<int, 0>{});
                 step(kt + 1, std::integral_constant<int, 1>{});
             }
@@ -323,12 +356,44 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // chunks past K read the row's first chunk instead (in bounds), whose
     // values meet padding codes: 0 in the 2-bit and base-3 layouts, but -1 in
     // the 1-bit layout, so there only rows without padding run unguarded.
-    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 4) == 0 &&
+    // Unguarded steps need two whole units in every k-tile, and without the
+    // skip branch an even number of k-tiles.
+    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K &&
+                          (units % (kSkip ? 2 : 4)) == 0 &&
                           (LAYOUT != kLayout1Bit || K == units * C::UC);
     if (interior)
         run(std::integral_constant<bool, false>{});
     else
         run(std::integral_constant<bool, true>{});
+
+    if constexpr (KG > 1) {
+        // Groups 1..KG-1 hand their INT32 sums to group 0 through LDS (free
+        // again: the last step ended on a barrier), one 64-lane row per
+        // accumulator register, so the accesses are conflict-free. The sums
+        // are exact, so the split does not change any result.
+        constexpr int kRegs = C::FI * C::FJ * 16;
+        int32_t *red = reinterpret_cast<int32_t *>(smem + C::LUT);
+        if (kg > 0) {
+            int32_t *dst = red + ((kg - 1) * (WM * WN) + wave) * kRegs * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < C::FI; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((i * C::FJ + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        lds_barrier();
+        if (kg > 0) return;
+        for (int h = 1; h < KG; ++h) {
+            const int32_t *src = red + ((h - 1) * (WM * WN) + wave) * kRegs * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < C::FI; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * C::FJ + j) * 16 + r) * 64];
+        }
+    }
 
     // Epilogue. Fragment (i, j) register r of lane l holds D[n][m] with
     // m = l % 32 (token within fragment i) and n = 8 (r / 4) + 4 (l / 32) +
@@ -390,11 +455,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     }
 }
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, bool EVEN_K, typename YT>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs<YT> g) {
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG, bool EVEN_K,
+          typename YT>
+__global__ __launch_bounds__(64 * WM * WN * KG) void gemm_kernel(const GemmArgs<YT> g) {
     const int t = xcd_tile(blockIdx.x, g.tiles_m * g.tiles_n);
     if (t < 0) return;
-    gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, EVEN_K, YT>(g, t);
+    gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, KG, EVEN_K, YT>(g, t);
 }
 
 // The prefill shape in one launch: the first blocks cover the columns that
@@ -408,18 +474,18 @@ __global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, i
     const int b = blockIdx.x;
     if (b < blocks1) {
         const int t = xcd_tile(b, g1.tiles_m * g1.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 2, 4, 2, EVEN_K, YT>(g1, t);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 2, 4, 2, 1, EVEN_K, YT>(g1, t);
     } else {
         const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, EVEN_K, YT>(g2, t);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, 1, EVEN_K, YT>(g2, t);
     }
 }
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, typename YT>
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG = 1, typename YT>
 hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                             int64_t ldy, int32_t *acc, hipStream_t s) {
-    using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST>;
+    using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST, KG>;
     const int64_t rb = row_bytes_of(LAYOUT, K);
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const int64_t ntiles = (int64_t)tm * tn;
@@ -432,8 +498,9 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
         return hipGetLastError();
     };
     static int lds_even = 0, lds_odd = 0;
-    if (K % 16 == 0) return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, true, YT>, &lds_even);
-    return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, false, YT>, &lds_odd);
+    if (K % 16 == 0)
+        return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, true, YT>, &lds_even);
+    return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, false, YT>, &lds_odd);
 }
 
 // Tile configuration by problem size, chosen by timing on MI355X: large
@@ -441,24 +508,31 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
 // fill whole rounds of 256 CUs, the columns that do take 256 x 256 tiles and
 // the leftover columns smaller tiles (in the same launch when they make one
 // round of 256 x 128 tiles, else in a second launch), so no round runs mostly
-// idle.
+// idle. With few tiles and long rows (64 or more k-tiles), two groups of four
+// waves split each tile's k-tiles: twice the waves per CU for the same tile.
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                             int64_t ldy, int32_t *acc, hipStream_t s) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    const int64_t t_wide = tiles(256, 128);
+    const int64_t t_wide = tiles(256, 128), t_sq = tiles(128, 128), t_small = tiles(128, 64);
+    const int64_t units = row_bytes_of(LAYOUT, K) / GemmCfg<LAYOUT, 128, 64, 2, 2, 2>::LB;
+    const bool long_k = (units + 1) / 2 >= 64;
+#define BL_GEMM_TILE(...)                                                                    \
+    return launch_gemm_tile<LAYOUT, __VA_ARGS__>(xq, scale, packed, gamma, M, N, K, y, ldy, acc, \
+                                                 s)
     // 256 x 128 tiles when they make several rounds, or one round that keeps
-    // at least half of the 256 CUs busy (measured faster than two rounds of
-    // 128 x 128 tiles for the leftover columns of the prefill shape)
-    if (t_wide >= 512 || (t_wide >= 128 && t_wide <= 256))
-        return launch_gemm_tile<LAYOUT, 256, 128, 2, 4, 2>(xq, scale, packed, gamma, M, N, K, y,
-                                                           ldy, acc, s);
-    if (tiles(128, 128) >= 256)
-        return launch_gemm_tile<LAYOUT, 128, 128, 2, 2, 2>(xq, scale, packed, gamma, M, N, K, y,
-                                                           ldy, acc, s);
-    return launch_gemm_tile<LAYOUT, 128, 64, 2, 2, 2>(xq, scale, packed, gamma, M, N, K, y, ldy,
-                                                      acc, s);
+    // more than half of the 256 CUs busy (measured faster than two rounds of
+    // 128 x 128 tiles for the leftover columns of the prefill shape; at
+    // exactly half, one round of 128 x 128 tiles is faster)
+    if (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)) BL_GEMM_TILE(256, 128, 2, 4, 2);
+    if (long_k) {
+        if (t_small <= 256) BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
+        if (t_sq >= 160) BL_GEMM_TILE(128, 128, 2, 2, 2, 2);
+    }
+    if (t_sq >= 256) BL_GEMM_TILE(128, 128, 2, 2, 2);
+    BL_GEMM_TILE(128, 64, 2, 2, 2);
+#undef BL_GEMM_TILE
 }
 
 // Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in 256 x 128 tiles,

@@ -84,6 +84,9 @@ FWD_CASES = [
     # whole tiles over rows with padding codes (K = 976 in 1024-code rows): the
     # unguarded interior path must not run there (regression)
     (183, 478, 976), (256, 128, 976),
+    # long rows: two wave groups split the k-tiles (no padding: unguarded
+    # whole tiles; padding: guarded)
+    (140, 333, 8192), (140, 200, 9000),
 ]
 
 

@@ -161,6 +161,13 @@ FWD_CASES = [
     (4096, 4357, 64), (2048, 8200, 48), (2000, 11000, 48), (2048, 11008, 40),
     # many rows at M <= 4 (the four-wave weight-streaming launch shape)
     (2, 16400, 96), (1, 16384, 33),
+    # long rows (64 or more k-tiles) over few tiles: two wave groups split each
+    # tile's k-tiles in the GEMM (odd k-tile counts, ragged K, edge tiles; an
+    # odd number of base-3 units at K = 8192). Base-3 takes the chunked
+    # weight-streaming product for the narrower of these and the GEMM from
+    # chunks x rows > 16384 on.
+    (130, 300, 9001), (200, 520, 8192), (130, 256, 10400), (150, 700, 12001), (97, 64, 16384),
+    (130, 1900, 8192), (130, 2000, 10400),
 ]
 
 
@@ -177,17 +184,43 @@ def test_forward_stage_parity(bl, layout, M, N, K):
     gamma = np.float32(0.0161)
     packed = oracle.pack(codes, layout)
     g = torch.tensor([gamma, 0, 0, 0], dtype=torch.float32, device="cuda")
+    acc_ref = oracle.int_product(xq, codes)
+    y64 = oracle.epilogue(acc_ref, gamma, scale)
     for ydt in (torch.float32, torch.bfloat16):
         y, acc = bl.bitlinear_forward(dev(xq), dev(scale), dev(packed), g, N, K, layout, ydt,
                                       acc=True)
         torch.cuda.synchronize()
-        acc_ref = oracle.int_product(xq, codes)
         assert np.array_equal(to_np(acc), acc_ref), "INT32 accumulators differ"
-        y64 = oracle.epilogue(acc_ref, gamma, scale)
         if ydt == torch.float32:
             check_y_f32(to_np(y), y64)
         else:
             check_y_bf16(y_bits(y), y64)
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3", "1bit"])
+def test_forward_long_rows_sampled(bl, layout):
+    """1024 tokens x 2560 rows x K = 8200 (ragged): 128 x 128 tiles whose
+    k-tiles two wave groups split. Accumulators and bf16 outputs on 24 token
+    rows spread over every 128-token tile (first and last rows included)."""
+    M, N, K = 1024, 2560, 8200
+    banner(f"forward long rows {layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(8200)
+    if layout == "1bit":
+        codes = np.where(rng.random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    else:
+        codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    scale = rng.uniform(0.5, 30.0, size=M).astype(np.float32)
+    gamma = np.float32(0.0123)
+    g = torch.tensor([gamma, 0, 0, 0], dtype=torch.float32, device="cuda")
+    y, acc = bl.bitlinear_forward(dev(xq), dev(scale), dev(oracle.pack(codes, layout)), g, N, K,
+                                  layout, torch.bfloat16, acc=True)
+    torch.cuda.synchronize()
+    rows = np.concatenate([[0, M - 1], 128 * np.arange(8) + rng.integers(0, 128, size=8),
+                           rng.choice(M, 14, replace=False)])
+    acc_ref = oracle.int_product(xq[rows], codes)
+    assert np.array_equal(to_np(acc)[rows], acc_ref), "INT32 accumulators differ"
+    check_y_bf16(y_bits(y)[rows], oracle.epilogue(acc_ref, gamma, scale[rows]))
 
 
 # ----------------------------------------------------------------------------
