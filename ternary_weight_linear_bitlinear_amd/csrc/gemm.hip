@@ -18,7 +18,9 @@
 //
 // Block tile BM tokens x BN weight rows, WM x WN waves, each owning
 // (BM/WM) x (BN/WN) outputs as 32 x 32 fragments. Loads run two k-tiles ahead
-// through two register sets; one barrier per k-tile. Blocks are mapped to
+// through two register sets; one barrier per k-tile. For long rows over few
+// tiles, KG groups of WM x WN waves split a tile's k-tiles and add their
+// INT32 sums through LDS before the epilogue. Blocks are mapped to
 // tiles so that each of the eight XCDs (dispatched round-robin by block id)
 // works on a contiguous run of tiles sharing activation rows in its L2.
 #include "bl_internal.hpp"
