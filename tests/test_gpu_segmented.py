@@ -56,6 +56,9 @@ FWD_CASES = [
     # (M, segments, K): skinny (M <= 16), tiled GEMM (M > 16), ragged rows and K
     (1, (64, 48, 80), 256), (4, (100, 36, 120), 200), (16, (16, 16, 16), 1000),
     (9, (3, 5, 7, 11, 13, 17, 19, 23), 96), (40, (100, 36, 120), 200), (300, (64, 48, 80), 333),
+    # long rows in the GEMM: two wave groups split the k-tiles (ragged K: the
+    # guarded path; K = 8192: whole tiles unguarded)
+    (130, (600, 400, 1000), 9000), (200, (520, 1000, 300), 8192),
 ]
 
 
