@@ -258,7 +258,7 @@ hipError_t launch_bwd(const uint16_t *A, int64_t lda, const void *B, int64_t ldb
     const int ti = (int)((I + G::BI - 1) / G::BI), tj = (int)((J + G::BJ - 1) / G::BJ);
     const int64_t blocks = ((int64_t)ti * tj + kXcds - 1) / kXcds * kXcds;
     auto kern = bwd_gemm_kernel<A_T, BSRC>;
-    static int lds_raised = 0;
+    static LdsFlag lds_raised{0};
     hipError_t e = allow_dynamic_lds(kern, G::SMEM, &lds_raised);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(G::kThreads), G::SMEM, s, A, lda, B,

@@ -25,23 +25,31 @@ constexpr int kBF16 = 1;
 constexpr int64_t kSkinnyMaxM = 16;
 
 // Kernels using more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-// must raise their limit once, to what the kernel's static LDS leaves free
-// (asking for all 160 KiB fails when the kernel also has static arrays).
-// `done` is a flag owned by the caller, one per kernel; setting the attribute
-// twice is harmless, so a race is benign. A request above the free space is
-// refused here instead of failing at launch.
+// must raise their limit, to what the kernel's static LDS leaves free (asking
+// for all 160 KiB fails when the kernel also has static arrays), once per
+// kernel and device. `done` is owned by the caller, one per kernel, with one
+// bit per device (devices past 63 set the attribute on every call). Setting
+// the attribute twice is harmless, so two threads racing here only repeat
+// the call. A request above the free space is refused here instead of
+// failing at launch.
+using LdsFlag = std::atomic<uint64_t>;
 template <typename F>
-hipError_t allow_dynamic_lds(F *kernel, size_t bytes, int *done) {
-    if (bytes <= 65536 || *done) return hipSuccess;
+hipError_t allow_dynamic_lds(F *kernel, size_t bytes, LdsFlag *done) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+    if (bit != 0 && (done->load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
     constexpr size_t kLdsBytes = 160 * 1024;
     hipFuncAttributes attr{};
-    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel));
+    e = hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel));
     if (e != hipSuccess) return e;
     if (attr.sharedSizeBytes + bytes > kLdsBytes) return hipErrorInvalidValue;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)(kLdsBytes - attr.sharedSizeBytes));
-    if (e == hipSuccess) *done = 1;
+    if (e == hipSuccess && bit != 0) done->fetch_or(bit, std::memory_order_release);
     return e;
 }
 

@@ -493,13 +493,13 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
     const int64_t ntiles = (int64_t)tm * tn;
     const int64_t blocks = (ntiles + kXcds - 1) / kXcds * kXcds;
     const GemmArgs<YT> g{xq, scale, packed, gamma, M, N, K, rb, tm, tn, y, ldy, acc};
-    auto launch = [&](auto kern, int *flag) {
+    auto launch = [&](auto kern, LdsFlag *flag) {
         hipError_t e = allow_dynamic_lds(kern, C::SMEM, flag);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::SMEM, s, g);
         return hipGetLastError();
     };
-    static int lds_even = 0, lds_odd = 0;
+    static LdsFlag lds_even{0}, lds_odd{0};
     if (K % 16 == 0)
         return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, true, YT>, &lds_even);
     return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, false, YT>, &lds_odd);
@@ -554,14 +554,14 @@ hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t 
                           K, rb, tm, tn2, y + n_main, N, acc ? acc + n_main : nullptr};
     const int blocks1 = (tm * tn1 + kXcds - 1) / kXcds * kXcds;
     const int blocks2 = (tm * tn2 + kXcds - 1) / kXcds * kXcds;
-    auto launch = [&](auto kern, int *flag) {
+    auto launch = [&](auto kern, LdsFlag *flag) {
         hipError_t e = allow_dynamic_lds(kern, C1::SMEM, flag);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)(blocks1 + blocks2)), dim3(C1::kThreads), C1::SMEM,
                            s, g1, blocks1, g2);
         return hipGetLastError();
     };
-    static int lds_even = 0, lds_odd = 0;
+    static LdsFlag lds_even{0}, lds_odd{0};
     if (K % 16 == 0) return launch(gemm_pair_kernel<LAYOUT, true, YT>, &lds_even);
     return launch(gemm_pair_kernel<LAYOUT, false, YT>, &lds_odd);
 }

@@ -143,7 +143,7 @@ hipError_t launch_lut_t(const int8_t *xq, const float *scale, const uint8_t *pac
                         const GammaMap &gamma, int64_t N, int64_t K, YT *y, int32_t *acc,
                         hipStream_t s) {
     auto kern = lut_gemv_kernel<YT>;
-    static int lds_raised = 0;
+    static LdsFlag lds_raised{0};
     hipError_t e = allow_dynamic_lds(kern, kLutSmem, &lds_raised);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)((N + kLutRows - 1) / kLutRows)), dim3(kLutThreads),

@@ -288,7 +288,7 @@ hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *
     dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)), (unsigned)((M + MAXM - 1) / MAXM)),
         block(64 * KS);
     auto kern = skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, YT>;
-    static int lds_raised = 0;  // one flag per instantiation of this launcher
+    static LdsFlag lds_raised{0};  // one flag per instantiation of this launcher
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, block, smem, s, xq, scale, packed, gamma, (int)M, N, K, rb, y,
@@ -616,7 +616,7 @@ hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &g
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (size_t)MAXM * (kRoundK + 16) +
                         2 * (size_t)RG * KS * 1024;
     auto kern = linear_decode_kernel<LAYOUT, KS, NSS, MAXM, STREAM, RG, XT, YT>;
-    static int lds_raised = 0;
+    static LdsFlag lds_raised{0};
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS), smem, s, x, packed, gamma,
