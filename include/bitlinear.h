@@ -32,8 +32,11 @@
  *    returns BL_ERR_DEVICE (the HIP error is consumed). Kernels that fault
  *    later surface at the caller's next synchronisation.
  *  - Non-finite inputs (NaN, Inf) are outside the contract.
- *  - Calls on different streams do not share state; the library holds no
- *    mutable global state.
+ *  - Calls may come from several host threads and streams. The library's
+ *    only process-wide state is per-device and set once: the result of the
+ *    architecture check, the compute-unit count and the raised LDS limit of
+ *    kernels that use more than 64 KiB, all kept in atomics. Concurrent calls
+ *    that write the same output buffers race like any other GPU work.
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
