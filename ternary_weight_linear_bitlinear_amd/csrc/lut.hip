@@ -128,9 +128,17 @@ __global__ __launch_bounds__(kLutThreads) void lut_gemv_kernel(
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (part != 0 || !row_ok) return;
-    float fs[kMaxSegments];
-    seg_factors(gm, gs, scale[0], fs);
-    const float v = (float)acc * seg_pick(gm, fs, n);
+    // one matrix: one factor; stacked segments pick the row's own (a
+    // wave-uniform branch, so the common case skips the selection)
+    float f;
+    if (gm.nseg == 1) {
+        f = gs[0] * scale[0] / 127.0f;
+    } else {
+        float fs[kMaxSegments];
+        seg_factors(gm, gs, scale[0], fs);
+        f = seg_pick(gm, fs, n);
+    }
+    const float v = (float)acc * f;
     if constexpr (sizeof(YT) == 4)
         y[n] = v;
     else

@@ -105,6 +105,38 @@ __device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut,
     }
 }
 
+// Epilogue of the decode products: four consecutive outputs n .. n + 3 of one
+// token (row pointers yt, acct) from their INT32 sums, y = acc * gamma *
+// scale / 127. A single matrix takes one factor; stacked segments pick each
+// row's own (a wave-uniform branch, so the common case skips the selection).
+template <typename YT>
+__device__ __forceinline__ void store_outputs(const GammaMap &gm,
+                                              const float (&gs)[kMaxSegments], float scale,
+                                              const v4i tot, int64_t n, int64_t N, YT *yt,
+                                              int32_t *acct) {
+    float f[4];
+    if (gm.nseg == 1) {
+        const float f0 = gs[0] * scale / 127.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = f0;
+    } else {
+        float fs[kMaxSegments];
+        seg_factors(gm, gs, scale, fs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = seg_pick(gm, fs, n + i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (n + i >= N) continue;
+        const float v = (float)tot[i] * f[i];
+        if constexpr (sizeof(YT) == 4)
+            yt[n + i] = v;
+        else
+            yt[n + i] = (YT)f32_to_bf16_rne(v);
+        if (acct) acct[n + i] = tot[i];
+    }
+}
+
 // RG row groups of 16 weight rows per workgroup share every activation read
 // from LDS (one operand load feeds RG matrix-core instructions); RG > 1 pays
 // off for batches, where activations outweigh the packed weights per row.
@@ -252,26 +284,15 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     for (int q = 0; q < RG; ++q) part[(q * KS + wave) * 64 + lane] = acc[q];
     lds_barrier();
     const int t = r;
-    float fs[kMaxSegments];
-    seg_factors(gm, gs, t < M ? scale[t] : 0.f, fs);
+    if (t >= M) return;
+    const float sc = scale[t];
     for (int q = wave; q < RG; q += KS) {  // wave q finishes row group q
         v4i tot = part[(q * KS) * 64 + lane];
 #pragma unroll
         for (int w = 1; w < KS; ++w) tot += part[(q * KS + w) * 64 + lane];
         // lane holds D[4g + i][r]: weight rows n0 + 16q + 4g + i, token r
-        if (t >= M) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t n = n0 + 16 * q + 4 * g + i;
-            if (n >= N) continue;
-            const int32_t a = tot[i];
-            const float v = (float)a * seg_pick(gm, fs, n);
-            if constexpr (sizeof(YT) == 4)
-                y[(int64_t)t * N + n] = v;
-            else
-                y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
-            if (acc_out) acc_out[(int64_t)t * N + n] = a;
-        }
+        store_outputs(gm, gs, sc, tot, n0 + 16 * q + 4 * g, N, y + (int64_t)t * N,
+                      acc_out ? acc_out + (int64_t)t * N : nullptr);
     }
 }
 
@@ -581,25 +602,12 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         lds_barrier();
         const int t = r;
         if (t < M) {
-            float fs[kMaxSegments];
-            seg_factors(gm, gs, tok_scale[t], fs);
             for (int q = wave; q < RG; q += KS) {  // wave q finishes row group q
                 v4i tot = pb[(q * KS) * 64 + lane];
 #pragma unroll
                 for (int w = 1; w < KS; ++w) tot += pb[(q * KS + w) * 64 + lane];
-                const int64_t n0 = (tile * RG + q) * 16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t n = n0 + 4 * g + i;
-                    if (n >= N) continue;
-                    const int32_t a = tot[i];
-                    const float v = (float)a * seg_pick(gm, fs, n);
-                    if constexpr (sizeof(YT) == 4)
-                        y[(int64_t)t * N + n] = v;
-                    else
-                        y[(int64_t)t * N + n] = (YT)f32_to_bf16_rne(v);
-                    if (acc_out) acc_out[(int64_t)t * N + n] = a;
-                }
+                store_outputs(gm, gs, tok_scale[t], tot, (tile * RG + q) * 16 + 4 * g, N,
+                              y + (int64_t)t * N, acc_out ? acc_out + (int64_t)t * N : nullptr);
             }
         }
         if constexpr (!STREAM) break;  // one tile per block
