@@ -407,6 +407,59 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     load_gammas(gm, gs);
     const bool one = gm.nseg == 1;
     const bool full = m0 + BM <= M && n0 + BN <= N && (ldy % 4) == 0;
+    if constexpr (sizeof(YT) == 2 && KG == 1 && BN >= 128) {
+        if (full && one && (ldy % 8) == 0) {
+            // Whole bf16 tiles of one matrix leave through LDS, one row of
+            // waves at a time:
+            // those waves write their outputs into the (now free) staging
+            // memory, then every thread stores 16-byte pieces of whole output
+            // rows, so each global store fills complete cache lines instead of
+            // scattering 8-byte pieces over 32 rows. Values and rounding are
+            // those of the direct stores. (Measured: 4096^3 68.7 -> 64.7 us;
+            // the narrow 128 x 64 tiles were slower this way and keep the
+            // direct stores.)
+            constexpr int RS = BN * 2 + 16;  // LDS bytes per output row (padded)
+            static_assert((BM / WM) * RS <= C::SMEM - C::LUT, "half tile fits the staging LDS");
+            uint8_t *ot = smem + C::LUT;
+            for (int h = 0; h < WM; ++h) {
+                if (wm == h) {
+#pragma unroll
+                    for (int i = 0; i < C::FI; ++i) {
+                        const int64_t m = m0 + wm * (BM / WM) + i * 32 + frow;
+                        const float f1 = gs[0] * scale[m] / 127.0f;
+#pragma unroll
+                        for (int j = 0; j < C::FJ; ++j) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int nl = wn * (BN / WN) + j * 32 + 8 * q + 4 * lg;
+                                const int64_t n = n0 + nl;
+                                const int32_t a0 = acc[i][j][4 * q], a1 = acc[i][j][4 * q + 1];
+                                const int32_t a2 = acc[i][j][4 * q + 2], a3 = acc[i][j][4 * q + 3];
+                                const bf16x2 lo = {(__bf16)((float)a0 * f1), (__bf16)((float)a1 * f1)};
+                                const bf16x2 hi = {(__bf16)((float)a2 * f1), (__bf16)((float)a3 * f1)};
+                                *reinterpret_cast<uint2 *>(ot + (i * 32 + frow) * RS + nl * 2) =
+                                    make_uint2(__builtin_bit_cast(uint32_t, lo),
+                                               __builtin_bit_cast(uint32_t, hi));
+                                if (acc_out)
+                                    *reinterpret_cast<int4 *>(acc_out + m * ldy + n) =
+                                        make_int4(a0, a1, a2, a3);
+                            }
+                        }
+                    }
+                }
+                lds_barrier();
+                constexpr int kPieces = (BM / WM) * (BN / 8);  // 16-byte pieces
+                for (int c = tid; c < kPieces; c += kThreads) {
+                    const int row = c / (BN / 8), pc = c % (BN / 8);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(ot + row * RS + pc * 16);
+                    *reinterpret_cast<uint4 *>(y + (m0 + h * (BM / WM) + row) * ldy + n0 +
+                                               pc * 8) = v;
+                }
+                lds_barrier();  // the next row of waves reuses the memory
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) {
         const int64_t m = m0 + wm * (BM / WM) + i * 32 + frow;
