@@ -237,10 +237,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
 
     // The loop is unrolled by U steps so that LDS buffers and register sets
     // are static and the compiler can wait for exactly the loads a step
-    // consumes. With one group and two register sets the body is free of
-    // branches: the k-tile count is rounded up to even, and loads of tiles
-    // past the end read valid addresses and are zeroed by the guards in
-    // load_tile, so those tiles add nothing.
+    // consumes. With one group the body is free of branches: pairs of steps,
+    // then one last step when the k-tile count is odd. Loads of tiles past
+    // the end read valid addresses (clamped, or zeroed by the guards in
+    // load_tile) and are never multiplied.
     //
     // With k-groups, group kg takes the k-tiles [k_lo, k_hi) of an equal
     // share. Every group runs the same number of steps, so the barriers
@@ -249,7 +249,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // valid addresses.
     constexpr int U = DIST > 2 ? DIST : 2;
     constexpr bool kSkip = KG > 1 || DIST > 2;
-    int64_t k_lo = 0, k_hi = ktiles, kt_end = (ktiles + 1) & ~(int64_t)1;
+    int64_t k_lo = 0, k_hi = ktiles, kt_end = ktiles;
     if constexpr (kSkip) {
         const int64_t share = (ktiles + KG - 1) / KG;
         k_lo = kg * share;
@@ -324,13 +324,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
                 store_a(stage0 + (L ^ 1) * C::STAGE, a_regs[(S + 1) % DIST]);
                 lds_barrier();
             };
-            for (int64_t kt = k_lo; kt < kt_end; kt += U) {
-                step(kt, std::integral_constant<int, 0>{});
-                step(kt + 1, std::integral_constant<int, 1 % DIST>{});
-                if constexpr (U == 4) {
-                    step(kt + 2, std::integral_constant<int, 2 % DIST>{});
-                    step(kt + 3, std::integral_constant<int, 3 % DIST>{});
+            if constexpr (kSkip) {
+                for (int64_t kt = k_lo; kt < kt_end; kt += U) {
+                    step(kt, std::integral_constant<int, 0>{});
+                    step(kt + 1, std::integral_constant<int, 1 % DIST>{});
+                    if constexpr (U == 4) {
+                        step(kt + 2, std::integral_constant<int, 2 % DIST>{});
+                        step(kt + 3, std::integral_constant<int, 3 % DIST>{});
+                    }
                 }
+            } else {
+                int64_t kt = k_lo;
+                for (; kt + 1 < k_hi; kt += 2) {
+                    step(kt, std::integral_constant<int, 0>{});
+                    step(kt + 1, std::integral_constant<int, 1>{});
+                }
+                if (kt < k_hi) step(kt, std::integral_constant<int, 0>{});
             }
         } else {
             // LDS holds tiles kt and kt+1; one register set carries tile kt+1.
@@ -347,9 +356,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
                 store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0]);
                 lds_barrier();
             };
-            for (int64_t kt = k_lo; kt < kt_end; kt += 2) {
-                step(kt, std::integral_constant<int, 0>{});
-                step(kt + 1, std::integral_constant<int, 1>{});
+            if constexpr (kSkip) {
+                for (int64_t kt = k_lo; kt < kt_end; kt += 2) {
+                    step(kt, std::integral_constant<int, 0>{});
+                    step(kt + 1, std::integral_constant<int, 1>{});
+                }
+            } else {
+                int64_t kt = k_lo;
+                for (; kt + 1 < k_hi; kt += 2) {
+                    step(kt, std::integral_constant<int, 0>{});
+                    step(kt + 1, std::integral_constant<int, 1>{});
+                }
+                if (kt < k_hi) step(kt, std::integral_constant<int, 0>{});
             }
         }
 
@@ -358,10 +376,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // chunks past K read the row's first chunk instead (in bounds), whose
     // values meet padding codes: 0 in the 2-bit and base-3 layouts, but -1 in
     // the 1-bit layout, so there only rows without padding run unguarded.
-    // Unguarded steps need two whole units in every k-tile, and without the
-    // skip branch an even number of k-tiles.
-    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K &&
-                          (units % (kSkip ? 2 : 4)) == 0 &&
+    // Unguarded steps need two whole units in every k-tile.
+    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 2) == 0 &&
                           (LAYOUT != kLayout1Bit || K == units * C::UC);
     if (interior)
         run(std::integral_constant<bool, false>{});

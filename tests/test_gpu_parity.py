@@ -168,6 +168,9 @@ FWD_CASES = [
     # chunks x rows > 16384 on.
     (130, 300, 9001), (200, 520, 8192), (130, 256, 10400), (150, 700, 12001), (97, 64, 16384),
     (130, 1900, 8192), (130, 2000, 10400),
+    # an odd number of k-tiles on whole tiles: the last step runs alone,
+    # unguarded (2-bit at K = 4224, base-3 at K = 5280: 33 k-tiles)
+    (256, 256, 4224), (256, 1100, 5280),
 ]
 
 
