@@ -89,7 +89,7 @@ bl_status forward_impl(const int8_t *xq, const float *scale, const uint8_t *pack
     bl_status st = device_ok();
     if (st != BL_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (bl::skinny_handles(M, N, layout))
+    if (bl::skinny_handles(M, N, K, layout))
         return launched(
             bl::launch_forward_skinny(xq, scale, packed, layout, gm, M, N, K, y, y_dtype, acc, s));
     return launched(

@@ -113,8 +113,8 @@ hipError_t launch_quant_acts(const void *x, int dtype, int64_t M, int64_t K,
 
 // ---- products (skinny.hip, gemm.hip) -------------------------------------
 // Whether the weight-streaming kernel (in 16-token chunks) or the tiled GEMM
-// takes an M x N product in `layout`.
-bool skinny_handles(int64_t M, int64_t N, int layout);
+// takes an M x N x K product in `layout`.
+bool skinny_handles(int64_t M, int64_t N, int64_t K, int layout);
 hipError_t launch_forward_skinny(const int8_t *xq, const float *scale,
                                  const uint8_t *packed, int layout,
                                  const GammaMap &gamma, int64_t M, int64_t N,

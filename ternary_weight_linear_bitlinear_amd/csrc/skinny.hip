@@ -733,17 +733,18 @@ hipError_t launch_forward_skinny(const int8_t *xq, const float *scale, const uin
 int64_t fused_decode_max_m() { return kFusedMaxM; }
 
 // Batches above 16 tokens stream the weights once per 16-token chunk (all
-// chunks in one launch). That beats the tiled GEMM while the chunks times the
-// rows stay small: with few token tiles the GEMM keeps only N/64 blocks busy,
-// each walking all of K. Crossovers measured on MI355X (K = 4096 and 11008):
-// 2-bit and 1-bit up to 6 chunks at 4096 rows, 4 at 11008-12288 rows and 2 at
-// 32768 rows; base-3, whose decode costs more per byte, up to 4 chunks at
-// 4096 rows, 2 at 11008-12288 and none at 32768.
-bool skinny_handles(int64_t M, int64_t N, int layout) {
+// chunks in one launch). That beats the tiled GEMM for a few chunks: with few
+// token tiles the GEMM keeps few blocks busy, each walking all of K, and long
+// rows (K >= 8192) favour the chunks further. Crossovers measured on MI355X
+// with the weights streamed from HBM (K = 4096 and 11008, N = 4096 to 32768):
+// 2-bit and 1-bit up to 3 chunks at any N, 6 at N <= 8192, 8 for long rows at
+// N <= 16384; base-3, whose decode costs more per byte, up to 3 chunks at
+// N <= 16384 and 5 at N <= 4096.
+bool skinny_handles(int64_t M, int64_t N, int64_t K, int layout) {
     if (M <= kSkinnyMaxM) return true;
     const int64_t chunks = (M + kSkinnyMaxM - 1) / kSkinnyMaxM;
-    if (layout == kLayoutBase3) return (chunks <= 2 && N <= 16384) || chunks * N <= 16384;
-    return chunks <= 2 || (chunks <= 6 && chunks * N <= 49152);
+    if (layout == kLayoutBase3) return (N <= 4096 && chunks <= 5) || (N <= 16384 && chunks <= 3);
+    return chunks <= 3 || (N <= 8192 && chunks <= 6) || (K >= 8192 && N <= 16384 && chunks <= 8);
 }
 
 hipError_t launch_linear_decode(const void *x, int x_dtype, const uint8_t *packed, int layout,

@@ -153,9 +153,10 @@ FWD_CASES = [
     (16, 100, 4096), (16, 33, 17), (17, 256, 256), (64, 130, 1000), (130, 300, 260),
     (257, 257, 320), (33, 1, 160), (128, 128, 4096), (300, 512, 129),
     # medium batches: the weight-streaming kernel in 16-token chunks (partial
-    # last chunk, six chunks) or, past the measured crossover, the GEMM (many
-    # rows; base-3 switches earlier than 2-bit)
+    # last chunk, six chunks, eight chunks over long rows) or, past the
+    # measured crossover, the GEMM (many rows; base-3 switches earlier)
     (17, 4096, 512), (96, 512, 4096), (40, 20000, 64), (33, 17000, 100), (31, 40000, 32),
+    (64, 20000, 64), (120, 1000, 9000),
     # enough 256 x 256 tiles for a full round plus leftover columns (a second
     # launch, or one paired launch when the leftover fills a round of 256 x 128)
     (4096, 4357, 64), (2048, 8200, 48), (2000, 11000, 48), (2048, 11008, 40),
