@@ -169,10 +169,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     v4i a_regs[DIST][C::ACH];
     uint4 b_regs[DIST][C::FJ];
 
-    // Interior tiles (the whole tile inside M and N, full k-tiles; the exact
-    // conditions are stated where `interior` is set)
-    // load without guards: the k-tile index is clamped, so the prefetches past
-    // the last tile re-read a valid tile whose data is never used. Edge tiles
+    // Tiles whose rows hold whole k-tiles (the exact conditions are stated
+    // where `interior` is set) load without guards: the k-tile index is
+    // clamped, so the prefetches past the last tile re-read a valid tile whose
+    // data is never used, and token rows past M re-read row M - 1 (weight rows
+    // past N read row 0): each output depends only on its own token and weight
+    // row, so those rows only feed outputs that are never stored. Other tiles
     // zero out-of-range chunks: they read a valid address and select zero, so
     // no branch splits the load stream and the compiler can keep all of a
     // tile's loads in flight. Rows that are not a multiple of 16 bytes take a
@@ -188,7 +190,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
             const int64_t m = m0 + row, k = kc0 + col * 16;
             if (!G) {
                 // (a chunk is wholly below or above K: K % 16 == 0 here)
-                a_reg[i] = *reinterpret_cast<const v4i *>(xq + m * K + (k < K ? k : 0));
+                const int64_t mr = m < M ? m : M - 1;
+                a_reg[i] = *reinterpret_cast<const v4i *>(xq + mr * K + (k < K ? k : 0));
             } else if (EVEN_K) {
                 const bool ok = m < M && k < K;
                 const v4i v = *reinterpret_cast<const v4i *>(xq + (ok ? m * K + k : 0));
@@ -377,8 +380,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // values meet padding codes: 0 in the 2-bit and base-3 layouts, but -1 in
     // the 1-bit layout, so there only rows without padding run unguarded.
     // Unguarded steps need two whole units in every k-tile.
-    const bool interior = m0 + BM <= M && n0 + BN <= N && EVEN_K && (units % 2) == 0 &&
-                          (LAYOUT != kLayout1Bit || K == units * C::UC);
+    const bool interior =
+        EVEN_K && (units % 2) == 0 && (LAYOUT != kLayout1Bit || K == units * C::UC);
     if (interior)
         run(std::integral_constant<bool, false>{});
     else
