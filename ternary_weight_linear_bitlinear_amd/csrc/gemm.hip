@@ -33,6 +33,21 @@ namespace {
 
 constexpr int kXcds = 8;
 
+// How a launch treats the ends of its rows, fixed per launch:
+//  kWholeK   K % 16 == 0, every k-tile holds two whole units and (1-bit)
+//            rows carry no padding codes: loads need no guard;
+//  kGuardedK K % 16 == 0 otherwise: the last k-tile's data past K is zeroed
+//            where it is consumed;
+//  kRaggedK  K % 16 != 0: activation rows are read byte-wise.
+constexpr int kWholeK = 0, kGuardedK = 1, kRaggedK = 2;
+inline int gemm_k_mode(int layout, int64_t K) {
+    if (K % 16 != 0) return kRaggedK;
+    const int64_t units = row_bytes_of(layout, K) / (layout == kLayout1Bit ? 8 : 16);
+    const int64_t unit_codes = layout == kLayoutBase3 ? 80 : 64;
+    if (units % 2 != 0 || (layout == kLayout1Bit && K != units * unit_codes)) return kGuardedK;
+    return kWholeK;
+}
+
 template <int LAYOUT, int BM_, int BN_, int WM_, int WN_, int DIST_, int KG_ = 1>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -118,10 +133,11 @@ __device__ __forceinline__ int xcd_tile(int b, int ntiles) {
     return t < ntiles ? t : -1;
 }
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG, bool EVEN_K,
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG, int KMODE,
           typename YT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     using C = GemmCfg<LAYOUT, BM, BN, WM, WN, DIST, KG>;
+    constexpr bool EVEN_K = KMODE != kRaggedK;  // K % 16 == 0
     constexpr int kThreads = C::kThreads;
     constexpr int kGT = C::kGroupThreads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -158,12 +174,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     const int64_t ktiles = (units + 1) / 2;
     // this lane's weight rows (one per fragment column block)
     const uint8_t *b_src[C::FJ];
-    bool b_ok[C::FJ];
 #pragma unroll
     for (int j = 0; j < C::FJ; ++j) {
         const int64_t n = n0 + wn * (BN / WN) + j * 32 + frow;
-        b_ok[j] = n < N;
-        b_src[j] = packed + (b_ok[j] ? n : 0) * rb;
+        b_src[j] = packed + (n < N ? n : 0) * rb;
     }
 
     v4i a_regs[DIST][C::ACH];
@@ -174,11 +188,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // clamped, so the prefetches past the last tile re-read a valid tile whose
     // data is never used, and token rows past M re-read row M - 1 (weight rows
     // past N read row 0): each output depends only on its own token and weight
-    // row, so those rows only feed outputs that are never stored. Other tiles
-    // zero out-of-range chunks: they read a valid address and select zero, so
-    // no branch splits the load stream and the compiler can keep all of a
-    // tile's loads in flight. Rows that are not a multiple of 16 bytes take a
-    // byte-wise path.
+    // row, so those rows only feed outputs that are never stored. Guarded
+    // tiles (data past K in their last k-tile) read the same valid addresses
+    // and zero what lies past K where it is consumed, so no branch or select
+    // splits the load stream and the compiler keeps all of a tile's loads in
+    // flight. Rows that are not a multiple of 16 bytes take a byte-wise path.
     auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 *b_reg, auto guard_c) {
         constexpr bool G = decltype(guard_c)::value;
         if (!G) kt = kt < ktiles ? kt : ktiles - 1;
@@ -188,14 +202,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
             const int q = gtid + i * kGT;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             const int64_t m = m0 + row, k = kc0 + col * 16;
-            if (!G) {
-                // (a chunk is wholly below or above K: K % 16 == 0 here)
+            if (!G || EVEN_K) {
+                // (a chunk is wholly below or above K: K % 16 == 0 here;
+                // guarded tiles zero the chunks past K in store_a)
                 const int64_t mr = m < M ? m : M - 1;
                 a_reg[i] = *reinterpret_cast<const v4i *>(xq + mr * K + (k < K ? k : 0));
-            } else if (EVEN_K) {
-                const bool ok = m < M && k < K;
-                const v4i v = *reinterpret_cast<const v4i *>(xq + (ok ? m * K + k : 0));
-                a_reg[i] = ok ? v : v4i{0, 0, 0, 0};
             } else {
                 v4i v = {0, 0, 0, 0};
                 if (m < M && k < K) {
@@ -211,22 +222,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         const int64_t unit = kt * 2 + lg;
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
-            if (!G) {
-                b_reg[j] = load_b<LAYOUT>(b_src[j] + unit * C::LB);
-            } else {
-                const bool ok = b_ok[j] && unit < units;
-                const uint4 v = load_b<LAYOUT>(b_src[j] + (ok ? unit * C::LB : 0));
-                b_reg[j] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-            }
+            // guarded tiles read the row's first unit in place of units past
+            // the end and zero them before the multiply
+            const int64_t u = G && unit >= units ? 0 : unit;
+            b_reg[j] = load_b<LAYOUT>(b_src[j] + u * C::LB);
         }
     };
 
-    auto store_a = [&](int8_t *As, const v4i *a_reg) {
+    // Stage the activation registers of k-tile kt in LDS. Guarded tiles with
+    // 16-byte rows zero the chunks past K here, where the values are consumed
+    // (a select at the load would make the compiler wait for it there).
+    auto store_a = [&](int8_t *As, const v4i *a_reg, int64_t kt, auto guard_c) {
+        constexpr bool Z = decltype(guard_c)::value && EVEN_K;
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
             const int q = gtid + i * kGT;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
-            *reinterpret_cast<v4i *>(As + row * C::LDSK + col * 16) = a_reg[i];
+            v4i v = a_reg[i];
+            if constexpr (Z) {
+                if (kt * C::BK + col * 16 >= K) v = v4i{0, 0, 0, 0};
+            }
+            *reinterpret_cast<v4i *>(As + row * C::LDSK + col * 16) = v;
+        }
+    };
+    // Guarded tiles: weight units past the row's end multiply as zero codes.
+    auto zero_units = [&](uint4 (&bu)[C::FJ], int64_t kt, auto guard_c) {
+        if constexpr (decltype(guard_c)::value) {
+            if (kt * 2 + lg >= units) {
+#pragma unroll
+                for (int j = 0; j < C::FJ; ++j) bu[j] = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
     };
 
@@ -314,7 +339,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
             // tile kt, LDS buffer S % 2.
 #pragma unroll
             for (int d = 0; d < DIST; ++d) load_tile(k_lo + d, a_regs[d], b_regs[d], guard_c);
-            store_a(stage0, a_regs[0]);
+            store_a(stage0, a_regs[0], k_lo, guard_c);
             __syncthreads();  // tile k_lo (and the decode table) ready
             auto step = [&](int64_t kt, auto set_c) {
                 constexpr int S = decltype(set_c)::value;
@@ -323,8 +348,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     #pragma unroll
                 for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[S][j];
                 load_tile(kt + DIST, a_regs[S], b_regs[S], guard_c);
+                zero_units(bu, kt, guard_c);
                 if (!kSkip || kt < k_hi) mma(stage0 + L * C::STAGE, bu);
-                store_a(stage0 + (L ^ 1) * C::STAGE, a_regs[(S + 1) % DIST]);
+                store_a(stage0 + (L ^ 1) * C::STAGE, a_regs[(S + 1) % DIST], kt + 1, guard_c);
                 lds_barrier();
             };
             if constexpr (kSkip) {
@@ -347,7 +373,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         } else {
             // LDS holds tiles kt and kt+1; one register set carries tile kt+1.
             load_tile(k_lo, a_regs[0], b_regs[0], guard_c);
-            store_a(stage0, a_regs[0]);
+            store_a(stage0, a_regs[0], k_lo, guard_c);
             __syncthreads();
             auto step = [&](int64_t kt, auto buf_c) {
                 constexpr int S = decltype(buf_c)::value;
@@ -355,8 +381,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     #pragma unroll
                 for (int j = 0; j < C::FJ; ++j) bu[j] = b_regs[0][j];
                 load_tile(kt + 1, a_regs[0], b_regs[0], guard_c);
+                zero_units(bu, kt, guard_c);
                 if (!kSkip || kt < k_hi) mma(stage0 + S * C::STAGE, bu);
-                store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0]);
+                store_a(stage0 + (S ^ 1) * C::STAGE, a_regs[0], kt + 1, guard_c);
                 lds_barrier();
             };
             if constexpr (kSkip) {
@@ -375,17 +402,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         }
 
     };
-    // Rows padded to whole units hold codes past K. Unguarded activation
-    // chunks past K read the row's first chunk instead (in bounds), whose
-    // values meet padding codes: 0 in the 2-bit and base-3 layouts, but -1 in
-    // the 1-bit layout, so there only rows without padding run unguarded.
-    // Unguarded steps need two whole units in every k-tile.
-    const bool interior =
-        EVEN_K && (units % 2) == 0 && (LAYOUT != kLayout1Bit || K == units * C::UC);
-    if (interior)
-        run(std::integral_constant<bool, false>{});
-    else
-        run(std::integral_constant<bool, true>{});
+    // The k-mode is fixed per launch (gemm_k_mode), so each kernel holds one
+    // load path and its registers are allocated for that path alone.
+    run(std::integral_constant<bool, KMODE != kWholeK>{});
 
     if constexpr (KG > 1) {
         // Groups 1..KG-1 hand their INT32 sums to group 0 through LDS (free
@@ -529,12 +548,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     }
 }
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG, bool EVEN_K,
+template <int LAYOUT, int BM, int BN, int WM, int WN, int DIST, int KG, int KMODE,
           typename YT>
 __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_kernel(const GemmArgs<YT> g) {
     const int t = xcd_tile(blockIdx.x, g.tiles_m * g.tiles_n);
     if (t < 0) return;
-    gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, KG, EVEN_K, YT>(g, t);
+    gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, KG, KMODE, YT>(g, t);
 }
 
 // The prefill shape in one launch: the first blocks cover the columns that
@@ -542,16 +561,16 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_kernel(const GemmArgs<
 // 256 x 128 tiles. Leftover tiles start as soon as CUs free up, so their
 // start-up overlaps the output writes of the large tiles (and no second
 // launch is waited for).
-template <int LAYOUT, bool EVEN_K, typename YT>
+template <int LAYOUT, int KMODE, typename YT>
 __global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, int blocks1,
                                                         const GemmArgs<YT> g2) {
     const int b = blockIdx.x;
     if (b < blocks1) {
         const int t = xcd_tile(b, g1.tiles_m * g1.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 2, 4, 2, 1, EVEN_K, YT>(g1, t);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 2, 4, 2, 1, KMODE, YT>(g1, t);
     } else {
         const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, 1, EVEN_K, YT>(g2, t);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, 1, KMODE, YT>(g2, t);
     }
 }
 
@@ -571,10 +590,17 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::SMEM, s, g);
         return hipGetLastError();
     };
-    static LdsFlag lds_even{0}, lds_odd{0};
-    if (K % 16 == 0)
-        return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, true, YT>, &lds_even);
-    return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, false, YT>, &lds_odd);
+    static LdsFlag lds_flag[3];  // one per k-mode
+    switch (gemm_k_mode(LAYOUT, K)) {
+        case kWholeK:
+            return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, kWholeK, YT>, &lds_flag[0]);
+        case kGuardedK:
+            return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, kGuardedK, YT>,
+                          &lds_flag[1]);
+        default:
+            return launch(gemm_kernel<LAYOUT, BM, BN, WM, WN, DIST, KG, kRaggedK, YT>,
+                          &lds_flag[2]);
+    }
 }
 
 // Tile configuration by problem size, chosen by timing on MI355X: large
@@ -639,9 +665,12 @@ hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t 
                            s, g1, blocks1, g2);
         return hipGetLastError();
     };
-    static LdsFlag lds_even{0}, lds_odd{0};
-    if (K % 16 == 0) return launch(gemm_pair_kernel<LAYOUT, true, YT>, &lds_even);
-    return launch(gemm_pair_kernel<LAYOUT, false, YT>, &lds_odd);
+    static LdsFlag lds_flag[3];  // one per k-mode
+    switch (gemm_k_mode(LAYOUT, K)) {
+        case kWholeK: return launch(gemm_pair_kernel<LAYOUT, kWholeK, YT>, &lds_flag[0]);
+        case kGuardedK: return launch(gemm_pair_kernel<LAYOUT, kGuardedK, YT>, &lds_flag[1]);
+        default: return launch(gemm_pair_kernel<LAYOUT, kRaggedK, YT>, &lds_flag[2]);
+    }
 }
 
 template <int LAYOUT, typename YT>
