@@ -207,6 +207,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
                 // guarded tiles zero the chunks past K in store_a)
                 const int64_t mr = m < M ? m : M - 1;
                 a_reg[i] = *reinterpret_cast<const v4i *>(xq + mr * K + (k < K ? k : 0));
+            } else if (K % 4 == 0) {
+                // rows 4-byte aligned: four dword loads; dwords past K read
+                // the row's first one and are zeroed in store_a
+                const int64_t mr = m < M ? m : M - 1;
+                const int32_t *p = reinterpret_cast<const int32_t *>(xq + mr * K);
+                v4i v;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const int64_t kd = k + 4 * d;
+                    v[d] = p[(kd < K ? kd : 0) / 4];
+                }
+                a_reg[i] = v;
             } else {
                 v4i v = {0, 0, 0, 0};
                 if (m < M && k < K) {
@@ -229,9 +241,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
         }
     };
 
-    // Stage the activation registers of k-tile kt in LDS. Guarded tiles with
-    // 16-byte rows zero the chunks past K here, where the values are consumed
-    // (a select at the load would make the compiler wait for it there).
+    // Stage the activation registers of k-tile kt in LDS. Guarded tiles zero
+    // the chunks (dwords, for 4-byte rows) past K here, where the values are
+    // consumed (a select at the load would make the compiler wait for it).
     auto store_a = [&](int8_t *As, const v4i *a_reg, int64_t kt, auto guard_c) {
         constexpr bool Z = decltype(guard_c)::value && EVEN_K;
 #pragma unroll
@@ -239,8 +251,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
             const int q = gtid + i * kGT;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             v4i v = a_reg[i];
+            const int64_t kb = kt * C::BK + col * 16;
             if constexpr (Z) {
-                if (kt * C::BK + col * 16 >= K) v = v4i{0, 0, 0, 0};
+                if (kb >= K) v = v4i{0, 0, 0, 0};
+            }
+            if constexpr (KMODE == kRaggedK) {  // the dword path of load_tile
+                if (K % 4 == 0) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        if (kb + 4 * d >= K) v[d] = 0;
+                }
             }
             *reinterpret_cast<v4i *>(As + row * C::LDSK + col * 16) = v;
         }

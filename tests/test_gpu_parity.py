@@ -172,6 +172,9 @@ FWD_CASES = [
     # an odd number of k-tiles on whole tiles: the last step runs alone,
     # unguarded (2-bit at K = 4224, base-3 at K = 5280: 33 k-tiles)
     (256, 256, 4224), (256, 1100, 5280),
+    # rows of K % 16 != 0 bytes but 4-byte aligned (dword loads), beside the
+    # byte-wise odd K above
+    (300, 700, 2052), (257, 1000, 4100),
 ]
 
 
