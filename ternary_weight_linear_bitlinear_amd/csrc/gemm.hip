@@ -644,18 +644,24 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     // 256 x 128 tiles when they make several rounds, or one round that keeps
     // more than half of the 256 CUs busy (measured faster than two rounds of
     // 128 x 128 tiles for the leftover columns of the prefill shape; at
-    // exactly half, one round of 128 x 128 tiles is faster)
-    if (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)) BL_GEMM_TILE(256, 128, 2, 4, 2);
+    // exactly half, one round of 128 x 128 tiles is faster), and, except for
+    // base-3 (whose weight decode the 256 tokens of a tile share), their last
+    // row of tiles is at least three quarters full (384 tokens: 128-row tiles
+    // are faster)
+    const bool rows_fill = LAYOUT == kLayoutBase3 || M % 256 == 0 || M % 256 >= 192;
+    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)))
+        BL_GEMM_TILE(256, 128, 2, 4, 2);
     if (long_k) {
         if (t_small <= 256) BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
         if (t_sq >= 160) BL_GEMM_TILE(128, 128, 2, 2, 2, 2);
     }
     if (t_sq >= 256) BL_GEMM_TILE(128, 128, 2, 2, 2);
     if constexpr (LAYOUT != kLayoutBase3) {
-        // less than one round of 128 x 64 tiles: 64 x 64 tiles reach more CUs
-        // (256 x 4096 x 4096: 16.1 -> 11.9 us); a base-3 k-tile of 160 codes
+        // up to one and a half rounds of 128 x 64 tiles: 64 x 64 tiles reach
+        // more CUs or balance the rounds (256 x 4096 x 4096: 16.1 -> 11.9 us,
+        // 512 x 4096 x 4096: 17.6 -> 17.0 us); a base-3 k-tile of 160 codes
         // does not split evenly over 64-row tiles
-        if (t_small < 256) BL_GEMM_TILE(64, 64, 2, 2, 2);
+        if (t_small <= 384) BL_GEMM_TILE(64, 64, 2, 2, 2);
     }
     BL_GEMM_TILE(128, 64, 2, 2, 2);
 #undef BL_GEMM_TILE
