@@ -183,16 +183,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     v4i a_regs[DIST][C::ACH];
     uint4 b_regs[DIST][C::FJ];
 
-    // Tiles whose rows hold whole k-tiles (the exact conditions are stated
-    // where `interior` is set) load without guards: the k-tile index is
-    // clamped, so the prefetches past the last tile re-read a valid tile whose
-    // data is never used, and token rows past M re-read row M - 1 (weight rows
-    // past N read row 0): each output depends only on its own token and weight
-    // row, so those rows only feed outputs that are never stored. Guarded
-    // tiles (data past K in their last k-tile) read the same valid addresses
-    // and zero what lies past K where it is consumed, so no branch or select
-    // splits the load stream and the compiler keeps all of a tile's loads in
-    // flight. Rows that are not a multiple of 16 bytes take a byte-wise path.
+    // Launches whose rows hold whole k-tiles (k-mode kWholeK, see
+    // gemm_k_mode) load without guards: the k-tile index is clamped, so the
+    // prefetches past the last tile re-read a valid tile whose data is never
+    // used, and token rows past M re-read row M - 1 (weight rows past N read
+    // row 0): each output depends only on its own token and weight row, so
+    // those rows only feed outputs that are never stored. Guarded launches
+    // (data past K in the last k-tile) read the same valid addresses and zero
+    // what lies past K where it is consumed, so no branch or select splits the
+    // load stream and the compiler keeps all of a tile's loads in flight. Rows
+    // that are not a multiple of 16 bytes load dwords (K % 4 == 0) or bytes.
     auto load_tile = [&](int64_t kt, v4i *a_reg, uint4 *b_reg, auto guard_c) {
         constexpr bool G = decltype(guard_c)::value;
         if (!G) kt = kt < ktiles ? kt : ktiles - 1;
@@ -287,8 +287,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
     // are static and the compiler can wait for exactly the loads a step
     // consumes. With one group the body is free of branches: pairs of steps,
     // then one last step when the k-tile count is odd. Loads of tiles past
-    // the end read valid addresses (clamped, or zeroed by the guards in
-    // load_tile) and are never multiplied.
+    // the end read valid addresses and are never multiplied.
     //
     // With k-groups, group kg takes the k-tiles [k_lo, k_hi) of an equal
     // share. Every group runs the same number of steps, so the barriers
