@@ -96,7 +96,8 @@ typedef enum { BL_TERNARY = 0, BL_BINARY = 1 } bl_scheme;
 int64_t bitlinear_packed_row_bytes(int64_t K, int layout);
 
 /* Device workspace (bytes) bitlinear_pack_weights needs for an N x K matrix:
- * it holds the per-block partial sums of the two-pass mean reduction. */
+ * it holds the per-block partial sums of the two-pass mean reduction. 0 for
+ * N < 1, K < 1 or an N * K past the int64 range (shapes the pack refuses). */
 size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
 
 /* Quantise and pack a latent weight matrix ([QAT-en] "The Ternary Weight

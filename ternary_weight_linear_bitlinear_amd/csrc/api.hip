@@ -124,7 +124,7 @@ int64_t bitlinear_packed_row_bytes(int64_t K, int layout) {
 }
 
 size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
-    if (N < 1 || K < 1) return 0;
+    if (N < 1 || K < 1 || N > INT64_MAX / K) return 0;
     return bl::pack_workspace_bytes(N * K);
 }
 

@@ -51,6 +51,7 @@ def test_row_bytes(bl):
     assert bl.bitlinear_packed_row_bytes(4096, "1bit") == 512
     assert bl.bitlinear_pack_workspace_bytes(0, 5) == 0
     assert bl.bitlinear_pack_workspace_bytes(4096, 4096) % 16 == 0
+    assert bl.bitlinear_pack_workspace_bytes(1 << 40, 1 << 30) == 0  # N * K past int64
 
 
 P = 0x10000  # a fake, 16-byte aligned address: never dereferenced on these paths
