@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--only", default="", help="comma list of rows to run (profiling runs)")
     ap.add_argument("--mode", default="full", choices=["full", "profile"],
                     help="profile: only the fused decode kernel (64 launches over rotating "
-                         "weight copies) and a 512 MiB device copy, for counter runs")
+                         "weight copies; with --only prefill, 8 launches of the 2-bit prefill "
+                         "GEMM instead) and a 512 MiB device copy, for counter runs")
     return ap.parse_args()
 
 
@@ -125,14 +126,22 @@ def main():
     rows = {}
 
     if args.mode == "profile":
-        p = synth.workload("decode")
-        W = to_dev(p.w_store, True)
-        x = to_dev(p.x_store, True)
-        packed, gamma = bl.bitlinear_pack_weights(W, "2bit")
-        copies = [packed.clone() for _ in range(args.copies)]
-        y = torch.empty((1, p.N), dtype=torch.float32, device=dev)
-        for i in range(64):
-            bl.bitlinear_linear(x, copies[i % args.copies], gamma, p.N, "2bit", y=y)
+        if "prefill" in only:
+            q = synth.workload("prefill")
+            xq, sc = bl.bitlinear_quant_acts(to_dev(q.x_store, True))
+            packed, gamma = bl.bitlinear_pack_weights(to_dev(q.w_store, True), "2bit")
+            y = torch.empty((q.M, q.N), dtype=torch.bfloat16, device=dev)
+            for i in range(8):
+                bl.bitlinear_forward(xq, sc, packed, gamma, q.N, q.K, "2bit", torch.bfloat16, y=y)
+        else:
+            p = synth.workload("decode")
+            W = to_dev(p.w_store, True)
+            x = to_dev(p.x_store, True)
+            packed, gamma = bl.bitlinear_pack_weights(W, "2bit")
+            copies = [packed.clone() for _ in range(args.copies)]
+            y = torch.empty((1, p.N), dtype=torch.float32, device=dev)
+            for i in range(64):
+                bl.bitlinear_linear(x, copies[i % args.copies], gamma, p.N, "2bit", y=y)
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(4):
