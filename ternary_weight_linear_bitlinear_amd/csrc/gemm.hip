@@ -694,9 +694,20 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)))
         BL_GEMM_TILE(256, 128, 2, 4, 2);
     if (long_k) {
+        if constexpr (LAYOUT != kLayoutBase3) {
+            // at most half a round of 128 x 64 tiles: 64 x 64 tiles, also
+            // with split k-tiles, reach twice the CUs (256 x 4096 x 11008:
+            // 37.2 -> 25.7 us)
+            if (t_small <= 128 && tiles(64, 64) <= 256) BL_GEMM_TILE(64, 64, 2, 2, 2, 2);
+        }
         if (t_small <= 256) BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
         if (t_sq >= 160) BL_GEMM_TILE(128, 128, 2, 2, 2, 2);
     }
+    // base-3, most of one round of 128 x 128 tiles: two groups split each
+    // tile's k-tiles (768 x 4096 x 4096: 30.4 -> 29.0 us, 640 x 4096 x 4096:
+    // 29.9 -> 28.9 us; under 160 tiles the split was slower)
+    if (LAYOUT == kLayoutBase3 && t_sq >= 160 && t_sq <= 256)
+        BL_GEMM_TILE(128, 128, 2, 2, 2, 2);
     if (t_sq >= 256) BL_GEMM_TILE(128, 128, 2, 2, 2);
     if constexpr (LAYOUT != kLayoutBase3) {
         // up to one and a half rounds of 128 x 64 tiles: 64 x 64 tiles reach

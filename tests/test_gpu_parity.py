@@ -175,6 +175,12 @@ FWD_CASES = [
     # rows of K % 16 != 0 bytes but 4-byte aligned (dword loads), beside the
     # byte-wise odd K above
     (300, 700, 2052), (257, 1000, 4100),
+    # base-3 with 160 to 256 tiles of 128 x 128: two groups split each tile's
+    # k-tiles (whole and ragged rows; 2-bit takes 64 x 64 tiles here)
+    (1280, 2048, 160), (1200, 2000, 333),
+    # long rows with at most half a round of 128 x 64 tiles: 2-bit takes
+    # 64 x 64 tiles with split k-tiles (edge tiles in both directions)
+    (250, 1000, 8200),
 ]
 
 
