@@ -679,7 +679,8 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int64_t t_wide = tiles(256, 128), t_sq = tiles(128, 128), t_small = tiles(128, 64);
     const int64_t units = row_bytes_of(LAYOUT, K) / GemmCfg<LAYOUT, 128, 64, 2, 2, 2>::LB;
-    const bool long_k = (units + 1) / 2 >= 64;
+    const int64_t ktiles = (units + 1) / 2;
+    const bool long_k = ktiles >= 64;
 #define BL_GEMM_TILE(...)                                                                    \
     return launch_gemm_tile<LAYOUT, __VA_ARGS__>(xq, scale, packed, gamma, M, N, K, y, ldy, acc, \
                                                  s)
@@ -703,6 +704,12 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
         if (t_small <= 256) BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
         if (t_sq >= 160) BL_GEMM_TILE(128, 128, 2, 2, 2, 2);
     }
+    // base-3, at most half a round of 128 x 64 tiles over 32 or more
+    // k-tiles: two groups split each tile's k-tiles (250 x 1000 x 8200:
+    // 97.7 -> 78.5 us, 256 x 4096 x 6144: 31.1 -> 28.7 us; at 26 k-tiles,
+    // K = 4096, the split was 1-3% slower)
+    if (LAYOUT == kLayoutBase3 && t_small <= 128 && ktiles >= 32)
+        BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
     // base-3, most of one round of 128 x 128 tiles: two groups split each
     // tile's k-tiles (768 x 4096 x 4096: 30.4 -> 29.0 us, 640 x 4096 x 4096:
     // 29.9 -> 28.9 us; under 160 tiles the split was slower)
@@ -714,6 +721,11 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
         // more CUs or balance the rounds (256 x 4096 x 4096: 16.1 -> 11.9 us,
         // 512 x 4096 x 4096: 17.6 -> 17.0 us); a base-3 k-tile of 160 codes
         // does not split evenly over 64-row tiles
+        // at most one round of them over 32 or more k-tiles: two groups split
+        // each tile's k-tiles (192 x 3000 x 5000: 36.1 -> 29.4 us, 320 x 2048
+        // x 8000: 24.7 -> 20.3 us; over more than one round the split was
+        // 7-9% slower)
+        if (ktiles >= 32 && tiles(64, 64) <= 256) BL_GEMM_TILE(64, 64, 2, 2, 2, 2);
         if (t_small <= 384) BL_GEMM_TILE(64, 64, 2, 2, 2);
     }
     BL_GEMM_TILE(128, 64, 2, 2, 2);

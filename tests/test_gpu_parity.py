@@ -181,6 +181,10 @@ FWD_CASES = [
     # long rows with at most half a round of 128 x 64 tiles: 2-bit takes
     # 64 x 64 tiles with split k-tiles (edge tiles in both directions)
     (250, 1000, 8200),
+    # at most one round of 64 x 64 tiles (2-bit) or half a round of 128 x 64
+    # tiles (base-3) over 32 or more k-tiles: split k-tiles at K = 4096, on
+    # ragged rows and at K = 6000
+    (200, 1000, 4096), (192, 900, 5000), (200, 1000, 6000),
 ]
 
 
