@@ -87,6 +87,9 @@ FWD_CASES = [
     # long rows: two wave groups split the k-tiles (no padding: unguarded
     # whole tiles; padding: guarded)
     (140, 333, 8192), (140, 200, 9000),
+    # at most one round of 64 x 64 tiles over 32 k-tiles: split k-tiles on
+    # whole rows
+    (200, 1000, 4096),
 ]
 
 
