@@ -681,6 +681,11 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     const int64_t units = row_bytes_of(LAYOUT, K) / GemmCfg<LAYOUT, 128, 64, 2, 2, 2>::LB;
     const int64_t ktiles = (units + 1) / 2;
     const bool long_k = ktiles >= 64;
+    // k-tiles from which two groups splitting them pay off on few tiles (see
+    // below); rows of K % 16 != 0 bytes load piecewise, take longer per
+    // k-tile and gain from 16 on (200 x 2000 x 3000: 2-bit 23.2 -> 19.5 us,
+    // base-3 39.7 -> 34.5 us)
+    const int64_t split_kt = K % 16 != 0 ? 16 : 32;
 #define BL_GEMM_TILE(...)                                                                    \
     return launch_gemm_tile<LAYOUT, __VA_ARGS__>(xq, scale, packed, gamma, M, N, K, y, ldy, acc, \
                                                  s)
@@ -704,11 +709,11 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
         if (t_small <= 256) BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
         if (t_sq >= 160) BL_GEMM_TILE(128, 128, 2, 2, 2, 2);
     }
-    // base-3, at most half a round of 128 x 64 tiles over 32 or more
+    // base-3, at most half a round of 128 x 64 tiles over split_kt or more
     // k-tiles: two groups split each tile's k-tiles (250 x 1000 x 8200:
     // 97.7 -> 78.5 us, 256 x 4096 x 6144: 31.1 -> 28.7 us; at 26 k-tiles,
     // K = 4096, the split was 1-3% slower)
-    if (LAYOUT == kLayoutBase3 && t_small <= 128 && ktiles >= 32)
+    if (LAYOUT == kLayoutBase3 && t_small <= 128 && ktiles >= split_kt)
         BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
     // base-3, most of one round of 128 x 128 tiles: two groups split each
     // tile's k-tiles (768 x 4096 x 4096: 30.4 -> 29.0 us, 640 x 4096 x 4096:
@@ -721,11 +726,11 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
         // more CUs or balance the rounds (256 x 4096 x 4096: 16.1 -> 11.9 us,
         // 512 x 4096 x 4096: 17.6 -> 17.0 us); a base-3 k-tile of 160 codes
         // does not split evenly over 64-row tiles
-        // at most one round of them over 32 or more k-tiles: two groups split
+        // at most one round of them over split_kt or more k-tiles: two groups split
         // each tile's k-tiles (192 x 3000 x 5000: 36.1 -> 29.4 us, 320 x 2048
         // x 8000: 24.7 -> 20.3 us; over more than one round the split was
         // 7-9% slower)
-        if (ktiles >= 32 && tiles(64, 64) <= 256) BL_GEMM_TILE(64, 64, 2, 2, 2, 2);
+        if (ktiles >= split_kt && tiles(64, 64) <= 256) BL_GEMM_TILE(64, 64, 2, 2, 2, 2);
         if (t_small <= 384) BL_GEMM_TILE(64, 64, 2, 2, 2);
     }
     BL_GEMM_TILE(128, 64, 2, 2, 2);

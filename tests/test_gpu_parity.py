@@ -185,6 +185,8 @@ FWD_CASES = [
     # tiles (base-3) over 32 or more k-tiles: split k-tiles at K = 4096, on
     # ragged rows and at K = 6000
     (200, 1000, 4096), (192, 900, 5000), (200, 1000, 6000),
+    # ragged rows split from 16 k-tiles on
+    (200, 2000, 3000),
 ]
 
 
