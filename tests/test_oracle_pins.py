@@ -98,6 +98,48 @@ def test_absmean_exact(shape, seed):
 
 
 # ----------------------------------------------------------------------------
+# 1-bit codes: centred by the mean alpha, not by zero
+def test_binary_codes_hand_example():
+    """[QAT-en] 'The BitLinear Recipe', step 2: alpha is the mean of the
+    weights; weights above it become +1, weights below it -1; step 4 rescales
+    by beta = mean|W|. Worked by hand: w = [1, 2, 3, 4, 5] has alpha = 3 and
+    beta = 3, so the codes are [-1, -1, -1, +1, +1] (the weight equal to alpha
+    takes -1, the reading for a tie). Centring on zero instead of alpha would
+    give five +1 codes."""
+    w = f32([[1.0, 2.0, 3.0, 4.0, 5.0]])
+    codes, flags, alpha, beta = oracle.binary_codes(w)
+    assert alpha == np.float32(3.0) and beta == np.float32(3.0)
+    assert codes[0].tolist() == [-1, -1, -1, 1, 1]
+    assert flags[0].tolist() == [0, 0, 1, 0, 0]  # only the tie is flagged
+    # negative weights: alpha = -2, codes of -1 and 0 are +1 although -1 < 0
+    w = f32([[-5.0, -3.0, -1.0, 0.0, -1.0]])
+    codes, _, alpha, beta = oracle.binary_codes(w)
+    assert alpha == np.float32(-2.0) and beta == np.float32(2.0)
+    assert codes[0].tolist() == [-1, -1, 1, 1, 1]
+
+
+@pytest.mark.parametrize("seed,mu", [(0, 0.05), (1, -0.03)])
+def test_binary_codes_exact_centring(seed, mu):
+    """On a matrix whose mean is far from zero, every unflagged code is the
+    sign of w - alpha against the exact rational mean (many weights lie
+    between 0 and alpha, so a sign test around 0 fails here)."""
+    rng = np.random.default_rng(seed)
+    w = rng.normal(mu, 0.02, size=(12, 50)).astype(np.float32)
+    codes, flags, alpha, beta = oracle.binary_codes(w)
+    exact = sum(Fraction(float(v)) for v in w.ravel()) / w.size
+    ref = np.array([1 if Fraction(float(v)) > exact else -1 for v in w.ravel()],
+                   np.int8).reshape(w.shape)
+    between = ((w > 0) & (w.astype(np.float64) < float(exact))) | \
+              ((w < 0) & (w.astype(np.float64) > float(exact)))
+    assert between.sum() > 50  # the case discriminates centring
+    ok = flags == 0
+    assert ok.sum() >= w.size - 2
+    assert np.array_equal(codes[ok], ref[ok])
+    exact_abs = sum(Fraction(float(v)) for v in np.abs(w).ravel()) / w.size
+    assert beta == frac_to_f32_rne(exact_abs)
+
+
+# ----------------------------------------------------------------------------
 # Ternary codes: the threshold form and the code set
 def _threshold_codes_exact(w: np.ndarray, d: np.float32):
     """[QAT-en] 'The Ternary Weight Recipe', equivalent form: |w| <= d/2 -> 0,
@@ -356,6 +398,47 @@ def test_quant_acts_invariants():
         ok = flags[m] == 0
         assert np.array_equal(xq[m][ok], np.rint(exact[ok]).astype(np.int8))
     assert scale[5] == np.float32(1e-6) and not xq[5].any()
+
+
+def _planted_ties():
+    """Rows whose fp32 steps x / s, then * 127 land exactly on k + 1/2 for
+    k = 0..126 (found by searching the float32 neighbourhood of (k + 1/2) s /
+    127; s is the row's largest |x|, planted as the first element)."""
+    rows, ks = [], []
+    for s in (np.float32(127.0), np.float32(20.0), np.float32(3.0)):
+        row, krow = [s], [None]
+        for k in range(127):
+            target = np.float32(k + 0.5)
+            x0 = np.float32(target * s / np.float32(127))
+            for d in (0, 1, -1, 2, -2, 3, -3):
+                x = x0
+                for _ in range(abs(d)):
+                    x = np.nextafter(x, np.float32(np.inf if d > 0 else -np.inf))
+                if abs(x) <= s and np.float32(np.float32(x / s) * np.float32(127)) == target:
+                    row += [x, -x]
+                    krow += [k, -k - 1]  # -x lands on -(k + 1/2), between -k-1 and -k
+                    break
+        rows.append((np.array(row, np.float32), krow))
+    return rows
+
+
+def test_quant_acts_ties_round_half_to_even():
+    """[b158] §3.2 and §5.2 round with torch.round, which rounds a value
+    exactly halfway between two integers to the even one. Planted elements
+    whose fp32 quotient times 127 is exactly k + 1/2 must give the even
+    neighbour (k for even k, k + 1 for odd k; mirrored for negative values),
+    not the neighbour away from zero."""
+    n_even = 0
+    for row, krow in _planted_ties():
+        xq, scale, flags = oracle.quant_acts(row[None, :])
+        assert scale[0] == row[0] and xq[0, 0] == 127
+        for j in range(1, row.size):
+            lo = krow[j]  # the value lies in (lo, lo + 1), exactly halfway
+            expect = lo if lo % 2 == 0 else lo + 1
+            assert xq[0, j] == expect, (row[0], row[j], lo, xq[0, j])
+            assert flags[0, j] == 1
+            n_even += (lo >= 0 and lo % 2 == 0)
+    assert n_even >= 150
 
 
 def test_quant_acts_outliers_hit_127():
