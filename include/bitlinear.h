@@ -229,11 +229,32 @@ bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8
 bl_status bitlinear_backward_weight(const void *grad_y, const void *x, int dtype, int64_t M,
                                     int64_t N, int64_t K, float *grad_w, void *stream);
 
+/* Dry run of the product dispatch: describes, without launching anything or
+ * touching device memory, the kernel launches bitlinear_forward (fused = 0)
+ * or bitlinear_linear with bf16 x (fused = 1) would enqueue for an M x N x K
+ * product in `layout` with output type y_dtype. The stacked (segmented)
+ * variants dispatch exactly as the plain calls with N = sum of the segments.
+ * One line per launch: the kernel instantiation as the profiler names it,
+ * then "grid=GXxGY block=THREADS lds=BYTES". Writes at most len - 1
+ * characters and a terminating NUL into buf (buf may be NULL when len is 0).
+ * Returns the number of launches (0 for M = 0 or N = 0), or -1 for arguments
+ * the call itself would refuse. Launch shapes that depend on the device's
+ * compute-unit count use the current device's, and assume none without a GPU.
+ * For tests and profiling: it lets a caller check which kernel configuration
+ * serves a shape. Host-only; safe to call from several threads. */
+int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int layout, int y_dtype, int fused,
+                           char *buf, size_t len);
+
 /* Human-readable name of a status code (static string). */
 const char *bitlinear_status_string(int status);
 
 /* Library version, (major << 16) | minor. */
 int bitlinear_version(void);
+
+/* Digest of the source files the library was built from (32 hex digits; a
+ * static string), so that a binding can refuse a library built from other
+ * sources than the ones beside it. "unknown" if the build did not set it. */
+const char *bitlinear_source_hash(void);
 
 #ifdef __cplusplus
 }

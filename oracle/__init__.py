@@ -71,6 +71,7 @@ def _load():
         "orc_ste_grad_x": (None, [_p, _p, ctypes.c_float, _i64, _i64, _i64, _p]),
         "orc_ste_grad_w": (None, [_p, _p, _i64, _i64, _i64, _p]),
         "orc_num_threads": (ctypes.c_int, []),
+        "orc_set_num_threads": (None, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -243,6 +244,11 @@ def ste_grad_w(grad_y: np.ndarray, x: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on."""
+    _load().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

@@ -375,6 +375,18 @@ void orc_ste_grad_w(const float *grad_y, const float *x, int64_t M, int64_t N,
 }
 
 /* Number of OpenMP threads the product loops would use (1 without OpenMP). */
+/* Threads the OpenMP loops above use from now on (the CPU baseline times
+ * the oracle on one thread and on all host threads). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

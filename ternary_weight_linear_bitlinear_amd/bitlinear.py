@@ -34,6 +34,25 @@ if not os.path.exists(LIB_PATH):
         "(there is no fallback path)")
 
 _lib = ctypes.CDLL(LIB_PATH)
+_lib.bitlinear_source_hash.restype = ctypes.c_char_p
+_lib.bitlinear_source_hash.argtypes = []
+
+
+def _refuse_stale_library() -> None:
+    """A library built from other sources than the ones beside it would be
+    tested and timed in their place: refuse it."""
+    from . import build as _build
+    if not os.path.isdir(_build.CSRC):
+        return  # an installed library without its sources: nothing to compare
+    built = _lib.bitlinear_source_hash().decode()
+    here = _build.source_hash()
+    if built != here:
+        raise ImportError(
+            f"{LIB_PATH} was built from other sources (library {built}, sources {here}): rebuild "
+            "it with `python -m ternary_weight_linear_bitlinear_amd.build`")
+
+
+_refuse_stale_library()
 _p, _i64, _int, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
 _lib.bitlinear_packed_row_bytes.restype = _i64
@@ -60,6 +79,8 @@ _lib.bitlinear_backward_input.restype = _int
 _lib.bitlinear_backward_input.argtypes = [_p, _int, _p, _int, _p, _i64, _i64, _i64, _p, _p]
 _lib.bitlinear_backward_weight.restype = _int
 _lib.bitlinear_backward_weight.argtypes = [_p, _p, _int, _i64, _i64, _i64, _p, _p]
+_lib.bitlinear_forward_plan.restype = _int
+_lib.bitlinear_forward_plan.argtypes = [_i64, _i64, _i64, _int, _int, _int, ctypes.c_char_p, _sz]
 _lib.bitlinear_status_string.restype = ctypes.c_char_p
 _lib.bitlinear_status_string.argtypes = [_int]
 _lib.bitlinear_version.restype = _int
@@ -69,7 +90,8 @@ EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
             "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
             "bitlinear_linear", "bitlinear_forward_segmented", "bitlinear_linear_segmented",
             "bitlinear_forward_lut", "bitlinear_backward_input", "bitlinear_backward_weight",
-            "bitlinear_status_string", "bitlinear_version"]
+            "bitlinear_forward_plan", "bitlinear_status_string", "bitlinear_version",
+            "bitlinear_source_hash"]
 FUSED_MAX_M = 4
 
 
@@ -113,6 +135,21 @@ def bitlinear_pack_workspace_bytes(N: int, K: int) -> int:
 
 def bitlinear_version() -> int:
     return int(_lib.bitlinear_version())
+
+
+def bitlinear_forward_plan(M: int, N: int, K: int, layout="2bit", out_dtype=torch.float32,
+                           fused: bool = False) -> list[str]:
+    """The kernel launches bitlinear_forward (or, with fused=True,
+    bitlinear_linear on bf16 x) would make for an M x N x K product, one
+    string per launch; nothing is launched."""
+    buf = ctypes.create_string_buffer(8192)
+    n = _lib.bitlinear_forward_plan(M, N, K, _layout(layout), _DTYPES[out_dtype], int(fused),
+                                    buf, len(buf))
+    if n < 0:
+        raise BitLinearError(BL_ERR_INVALID_ARG, "bitlinear_forward_plan")
+    lines = buf.value.decode().splitlines()
+    assert len(lines) == n
+    return lines
 
 
 def bitlinear_status_string(status: int) -> str:

@@ -10,6 +10,11 @@
 
 #include "bl_internal.hpp"
 
+// Digest of the sources this library was built from, set by the build script.
+#ifndef BL_SOURCE_HASH
+#define BL_SOURCE_HASH "unknown"
+#endif
+
 namespace {
 
 constexpr int64_t kMaxK = 2147483647LL / 127;  // 127 * K must fit in INT32
@@ -249,6 +254,41 @@ bl_status bitlinear_backward_weight(const void *grad_y, const void *x, int dtype
                                                s));
 }
 
+int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int layout, int y_dtype, int fused,
+                           char *buf, size_t len) {
+    if (M < 0 || N < 0 || K < 1 || K > kMaxK || N > 2147483647LL) return -1;
+    if (!valid_layout(layout) || !valid_dtype(y_dtype)) return -1;
+    if (fused ? M > bl::fused_decode_max_m() : M > 65535LL * 128) return -1;
+    bl::PlanSink sink;
+    if (M > 0 && N > 0) {
+        // stand-in addresses: with a sink installed nothing is launched and no
+        // pointer is dereferenced, only offset
+        const uintptr_t fake = 4096;
+        auto *xq = reinterpret_cast<const int8_t *>(fake);
+        auto *sc = reinterpret_cast<const float *>(fake);
+        auto *pk = reinterpret_cast<const uint8_t *>(fake);
+        const bl::GammaMap gm = bl::GammaMap::single(sc);
+        void *y = reinterpret_cast<void *>(fake);
+        bl::t_plan = &sink;
+        if (fused)
+            (void)bl::launch_linear_decode(y, BL_BF16, pk, layout, gm, M, N, K, y, y_dtype,
+                                           nullptr, nullptr);
+        else if (bl::skinny_handles(M, N, K, layout))
+            (void)bl::launch_forward_skinny(xq, sc, pk, layout, gm, M, N, K, y, y_dtype, nullptr,
+                                            nullptr);
+        else
+            (void)bl::launch_forward_gemm(xq, sc, pk, layout, gm, M, N, K, y, y_dtype, nullptr,
+                                          nullptr);
+        bl::t_plan = nullptr;
+    }
+    if (buf && len > 0) {
+        const size_t n = sink.text.size() < len - 1 ? sink.text.size() : len - 1;
+        std::memcpy(buf, sink.text.data(), n);
+        buf[n] = '\0';
+    }
+    return sink.launches;
+}
+
 const char *bitlinear_status_string(int status) {
     switch (status) {
         case BL_OK: return "ok";
@@ -259,6 +299,8 @@ const char *bitlinear_status_string(int status) {
     }
 }
 
-int bitlinear_version(void) { return (1 << 16) | 0; }
+int bitlinear_version(void) { return (1 << 16) | 1; }
+
+const char *bitlinear_source_hash(void) { return BL_SOURCE_HASH; }
 
 }  // extern "C"

@@ -4,10 +4,41 @@
 
 #include <hip/hip_runtime.h>
 #include <atomic>
+#include <cstdarg>
+#include <cstdio>
 #include <stddef.h>
 #include <stdint.h>
+#include <string>
 
 namespace bl {
+
+// Dry runs of the product dispatch (bitlinear_forward_plan). While a sink is
+// installed on the calling thread, the product launchers append one line per
+// launch they would make -- the kernel instantiation as the profiler names it,
+// the grid, the block and the dynamic LDS bytes -- and launch nothing.
+struct PlanSink {
+    std::string text;
+    int launches = 0;
+};
+inline thread_local PlanSink *t_plan = nullptr;
+
+// Appends "<kernel> grid=GXxGY block=B lds=S" to the installed sink.
+inline void plan_note(unsigned gx, unsigned gy, unsigned block, size_t lds, const char *fmt, ...) {
+    char name[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(name, sizeof name, fmt, ap);
+    va_end(ap);
+    char line[640];
+    snprintf(line, sizeof line, "%s grid=%ux%u block=%u lds=%zu\n", name, gx, gy, block, lds);
+    t_plan->text += line;
+    t_plan->launches += 1;
+}
+
+// Type names as the profiler prints kernel template arguments.
+template <typename T> constexpr const char *type_name();
+template <> constexpr const char *type_name<float>() { return "float"; }
+template <> constexpr const char *type_name<uint16_t>() { return "unsigned short"; }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

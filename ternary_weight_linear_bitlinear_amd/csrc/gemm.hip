@@ -652,6 +652,12 @@ hipError_t launch_gemm_tile(const int8_t *xq, const float *scale, const uint8_t 
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::SMEM, s, g);
         return hipGetLastError();
     };
+    if (t_plan) {
+        plan_note((unsigned)blocks, 1, C::kThreads, C::SMEM,
+                  "gemm_kernel<%d, %d, %d, %d, %d, %d, %d, %d, %s>", LAYOUT, BM, BN, WM, WN, DIST,
+                  KG, gemm_k_mode(LAYOUT, K), type_name<YT>());
+        return hipSuccess;
+    }
     static LdsFlag lds_flag[3];  // one per k-mode
     switch (gemm_k_mode(LAYOUT, K)) {
         case kWholeK:
@@ -763,6 +769,12 @@ hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t 
                            s, g1, blocks1, g2);
         return hipGetLastError();
     };
+    if (t_plan) {
+        plan_note((unsigned)(blocks1 + blocks2), 1, C1::kThreads, C1::SMEM,
+                  "gemm_pair_kernel<%d, %d, %s> (%d tiles 256x256 + %d tiles 256x128)", LAYOUT,
+                  gemm_k_mode(LAYOUT, K), type_name<YT>(), tm * tn1, tm * tn2);
+        return hipSuccess;
+    }
     static LdsFlag lds_flag[3];  // one per k-mode
     switch (gemm_k_mode(LAYOUT, K)) {
         case kWholeK: return launch(gemm_pair_kernel<LAYOUT, kWholeK, YT>, &lds_flag[0]);
@@ -784,6 +796,11 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
             const int64_t rounds = tm * tn / kCUs;
             int64_t tn_main = rounds * kCUs / tm;
             if (tn_main > tn) tn_main = tn;
+            // many row tiles over narrow columns (tm > 256, tm not a multiple
+            // of 256, one column of tiles) leave no whole round: no 256 x 256
+            // launch, all columns take the smaller tiles
+            if (tn_main == 0)
+                return launch_gemm_cols<LAYOUT>(xq, scale, packed, gamma, M, N, K, y, N, acc, s);
             const int64_t n_main = tn_main * 256 < N ? tn_main * 256 : N;
             const int64_t n_rest = N - n_main;
             const int64_t t_rest = tm * ((n_rest + 127) / 128);

@@ -314,6 +314,11 @@ hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *
     dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)), (unsigned)((M + MAXM - 1) / MAXM)),
         block(64 * KS);
     auto kern = skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, YT>;
+    if (t_plan) {
+        plan_note(grid.x, grid.y, block.x, smem, "skinny_kernel<%d, %d, %d, %d, %d, %s>", LAYOUT,
+                  KS, NSS, RG, MAXM, type_name<YT>());
+        return hipSuccess;
+    }
     static LdsFlag lds_raised{0};  // one flag per instantiation of this launcher
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
@@ -629,6 +634,12 @@ hipError_t launch_linear_m(const XT *x, const uint8_t *packed, const GammaMap &g
     const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (size_t)MAXM * (kRoundK + 16) +
                         2 * (size_t)RG * KS * 1024;
     auto kern = linear_decode_kernel<LAYOUT, KS, NSS, MAXM, STREAM, RG, XT, YT>;
+    if (t_plan) {
+        plan_note((unsigned)grid, 1, 64 * KS, smem,
+                  "linear_decode_kernel<%d, %d, %d, %d, %s, %d, %s, %s>", LAYOUT, KS, NSS, MAXM,
+                  STREAM ? "true" : "false", RG, type_name<XT>(), type_name<YT>());
+        return hipSuccess;
+    }
     static LdsFlag lds_raised{0};
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;

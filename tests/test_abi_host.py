@@ -219,3 +219,36 @@ def test_lut_rejects_and_limits(bl):
     assert f(layout=2) == bl.BL_ERR_UNSUPPORTED
     assert f(M=2) == bl.BL_ERR_UNSUPPORTED
     assert f(M=0) == bl.BL_OK and f(N=0) == bl.BL_OK
+
+
+def test_forward_plan_names_the_kernels(bl):
+    """The dry run of the dispatch names the launches, without a GPU, for
+    shapes whose launch shape does not depend on the compute-unit count."""
+    import torch
+    plan = bl.bitlinear_forward_plan(2048, 11008, 4096, "2bit", torch.bfloat16)
+    assert len(plan) == 1 and plan[0].startswith("gemm_pair_kernel<0, 0, unsigned short>")
+    assert "(256 tiles 256x256 + 176 tiles 256x128)" in plan[0]
+    plan = bl.bitlinear_forward_plan(4096, 4096, 4096, "2bit", torch.bfloat16)
+    assert plan == ["gemm_kernel<0, 256, 256, 2, 4, 2, 1, 0, unsigned short> grid=256x1 "
+                    "block=512 lds=" + plan[0].split("lds=")[1]]
+    plan = bl.bitlinear_forward_plan(1, 4096, 4096, "2bit", torch.float32, fused=True)
+    assert plan[0].startswith("linear_decode_kernel<0, 8, 2, 1, false, 1, unsigned short, float> "
+                              "grid=256x1 block=512")
+    plan = bl.bitlinear_forward_plan(16, 12288, 4096, "2bit", torch.bfloat16)
+    assert plan[0].startswith("skinny_kernel<0, 8, 2, 2, 16, unsigned short> grid=384x1")
+    assert bl.bitlinear_forward_plan(0, 5, 5) == []
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear_forward_plan(5, 4096, 4096, fused=True)
+
+
+@pytest.mark.parametrize("layout", ["2bit", "1bit", "base3"])
+@pytest.mark.parametrize("M,N", [(70000, 200), (70000, 256), (65600, 100), (300 * 256, 256)])
+def test_forward_plan_never_launches_an_empty_grid(bl, layout, M, N):
+    """Many row tiles over one column of tiles: no launch has zero blocks and
+    the launches cover every column (an M past 256 tiles of 256 rows that is
+    not a whole number of rounds once left a 256 x 256 launch over 0 columns)."""
+    plan = bl.bitlinear_forward_plan(M, N, 256, layout)
+    assert plan
+    for line in plan:
+        gx = int(line.split("grid=")[1].split("x")[0])
+        assert gx > 0, line

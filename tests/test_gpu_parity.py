@@ -169,9 +169,13 @@ FWD_CASES = [
     # chunks x rows > 16384 on.
     (130, 300, 9001), (200, 520, 8192), (130, 256, 10400), (150, 700, 12001), (97, 64, 16384),
     (130, 1900, 8192), (130, 2000, 10400),
-    # an odd number of k-tiles on whole tiles: the last step runs alone,
-    # unguarded (2-bit at K = 4224, base-3 at K = 5280: 33 k-tiles)
+    # 33 k-tiles over few tiles (2-bit at K = 4224, base-3 at K = 5280): two
+    # wave groups split them (2-bit 64 x 64 tiles, base-3 128 x 64)
     (256, 256, 4224), (256, 1100, 5280),
+    # an odd number of k-tiles on whole tiles under one wave group: the last
+    # step runs alone, unguarded (2-bit 64 x 64 tiles, 3 k-tiles; base-3 takes
+    # its guarded path at K = 384)
+    (300, 300, 384),
     # rows of K % 16 != 0 bytes but 4-byte aligned (dword loads), beside the
     # byte-wise odd K above
     (300, 700, 2052), (257, 1000, 4100),
@@ -237,6 +241,40 @@ def test_forward_long_rows_sampled(bl, layout):
     torch.cuda.synchronize()
     rows = np.concatenate([[0, M - 1], 128 * np.arange(8) + rng.integers(0, 128, size=8),
                            rng.choice(M, 14, replace=False)])
+    acc_ref = oracle.int_product(xq[rows], codes)
+    assert np.array_equal(to_np(acc)[rows], acc_ref), "INT32 accumulators differ"
+    check_y_bf16(y_bits(y)[rows], oracle.epilogue(acc_ref, gamma, scale[rows]))
+
+
+@pytest.mark.parametrize("layout,M,N,K,kernel", [
+    # one round of 128 x 128 tiles, one wave group, whole k-tiles
+    ("2bit", 1000, 4096, 4096, "gemm_kernel<0, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
+    ("1bit", 1000, 4096, 4096, "gemm_kernel<2, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
+    # many row tiles over one column of tiles, not a whole number of rounds
+    ("2bit", 70000, 200, 256, "gemm_kernel<0, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
+    ("1bit", 70000, 200, 256, "gemm_kernel<2, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
+    ("base3", 70000, 200, 256, "gemm_kernel<1, 256, 128, 2, 4, 2, 1, 0, unsigned short>"),
+])
+def test_forward_large_sampled(bl, layout, M, N, K, kernel):
+    """Dispatch cases too large for a full oracle product: the configuration is
+    asserted through the dispatch's dry run, accumulators and bf16 outputs are
+    compared on sampled token rows (first and last included), every column."""
+    banner(f"forward sampled {layout} M={M} N={N} K={K}")
+    plan = bl.bitlinear_forward_plan(M, N, K, layout, torch.bfloat16)
+    assert len(plan) == 1 and plan[0].split(" grid=")[0] == kernel, plan
+    rng = np.random.default_rng(M + N + K)
+    if layout == "1bit":
+        codes = np.where(rng.random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    else:
+        codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    scale = rng.uniform(0.5, 30.0, size=M).astype(np.float32)
+    gamma = np.float32(0.0137)
+    g = torch.tensor([gamma, 0, 0, 0], dtype=torch.float32, device="cuda")
+    y, acc = bl.bitlinear_forward(dev(xq), dev(scale), dev(oracle.pack(codes, layout)), g, N, K,
+                                  layout, torch.bfloat16, acc=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
     acc_ref = oracle.int_product(xq[rows], codes)
     assert np.array_equal(to_np(acc)[rows], acc_ref), "INT32 accumulators differ"
     check_y_bf16(y_bits(y)[rows], oracle.epilogue(acc_ref, gamma, scale[rows]))

@@ -13,7 +13,7 @@ import torch
 import oracle
 from ternary_weight_linear_bitlinear_amd import synth
 from parity_util import (SCALE_RTOL, check_codes, check_rel, check_y_bf16, check_y_f32,
-                         excluded_acc_mask, to_np)
+                         excluded_acc_mask, guarded, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,24 +54,37 @@ def test_random_shape_parity(bl, case):
     scheme = "binary" if layout == "1bit" else "ternary"
     p = synth.make_problem(M=M, N=N, K=K, seed=5000 + i, dtype=dtype, outlier_frac=0.01)
     bf = dtype == "bf16"
-    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, bf), layout, scheme)
+    # every output sits between guard bytes (checked after the calls)
+    packed, gpk = guarded((N, bl.bitlinear_packed_row_bytes(K, layout)), torch.uint8)
+    gamma, gg = guarded((1,), torch.float32)
+    bl.bitlinear_pack_weights(dev(p.w_store, bf), layout, scheme, packed=packed, gamma=gamma)
     x = dev(p.x_store, bf)
     ref = oracle.forward(p.w, p.x, layout, scheme)
+    torch.cuda.synchronize()
+    gpk.check("packed", all_written=False)  # any byte value is a valid code byte
+    gg.check("gamma")
     codes_gpu, bad = oracle.unpack(to_np(packed), K, layout)
     assert bad == 0
     check_codes(codes_gpu, ref["codes"], ref["wflags"], "codes")
+    y, gy_ = guarded((M, N), out_dtype)
+    acc, ga = guarded((M, N), torch.int32)
     if M <= 4:
-        y, acc = bl.bitlinear_linear(x, packed, gamma, N, layout, out_dtype, acc=True)
+        bl.bitlinear_linear(x, packed, gamma, N, layout, y=y, acc=acc)
         xq_bad = np.zeros_like(ref["xq"], bool)  # same fp32 steps as the oracle
     else:
-        xq, scale = bl.bitlinear_quant_acts(x)
-        y, acc = bl.bitlinear_forward(xq, scale, packed, gamma, N, K, layout, out_dtype,
-                                      acc=True)
+        xq, gq = guarded((M, K), torch.int8)
+        scale, gs = guarded((M,), torch.float32)
+        bl.bitlinear_quant_acts(x, xq=xq, scale=scale)
+        bl.bitlinear_forward(xq, scale, packed, gamma, N, K, layout, y=y, acc=acc)
         torch.cuda.synchronize()
+        gq.check("xq", all_written=False)  # codes may equal the pattern's byte
+        gs.check("scale")
         check_codes(to_np(xq), ref["xq"], ref["xflags"], "xq")
         assert np.array_equal(to_np(scale), ref["scale"])
         xq_bad = to_np(xq) != ref["xq"]
     torch.cuda.synchronize()
+    gy_.check("y")
+    ga.check("acc")
     ex = excluded_acc_mask(xq_bad, codes_gpu != ref["codes"])
     assert np.array_equal(to_np(acc)[~ex], ref["acc"][~ex])
     if out_dtype == torch.float32:
@@ -112,14 +125,17 @@ def test_random_stack_parity(bl, case):
     packed = dev(np.concatenate([oracle.pack(c, layout) for c in codes], axis=0), False)
     p = synth.make_problem(M=M, N=1, K=K, seed=9500 + i, dtype="bf16", outlier_frac=0.01)
     x = dev(p.x_store, True)
+    y, gy_ = guarded((M, sum(segs)), torch.float32)
+    acc, ga = guarded((M, sum(segs)), torch.int32)
     if M <= 4:
-        y, acc = bl.bitlinear_linear_segmented(x, packed, dev(scales, False), segs, layout,
-                                               acc=True)
+        bl.bitlinear_linear_segmented(x, packed, dev(scales, False), segs, layout, y=y, acc=acc)
     else:
         xq, scale = bl.bitlinear_quant_acts(x)
-        y, acc = bl.bitlinear_forward_segmented(xq, scale, packed, dev(scales, False), segs, K,
-                                                layout, acc=True)
+        bl.bitlinear_forward_segmented(xq, scale, packed, dev(scales, False), segs, K, layout,
+                                       y=y, acc=acc)
     torch.cuda.synchronize()
+    gy_.check("y")
+    ga.check("acc")
     xq_ref, s_ref, _ = oracle.quant_acts(p.x)  # same fp32 steps on both sides
     acc_ref = oracle.int_product(xq_ref, np.concatenate(codes, axis=0))
     assert np.array_equal(to_np(acc), acc_ref)
@@ -181,9 +197,13 @@ def test_random_backward_parity(bl, case):
     p = synth.make_problem(M=M, N=N, K=K, seed=8000 + i, dtype="bf16", grad_std=1e-3)
     packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, True), "2bit")
     gy = dev(p.grad_y_store, True)
-    gx = bl.bitlinear_backward_input(gy, packed, gamma, K)
-    gw = bl.bitlinear_backward_weight(gy, dev(p.x_store, True))
+    gx, ggx = guarded((M, K), torch.float32)
+    gw, ggw = guarded((N, K), torch.float32)
+    bl.bitlinear_backward_input(gy, packed, gamma, K, grad_x=gx)
+    bl.bitlinear_backward_weight(gy, dev(p.x_store, True), grad_w=gw)
     torch.cuda.synchronize()
+    ggx.check("grad_x")
+    ggw.check("grad_w")
     codes, bad = oracle.unpack(to_np(packed), K, "2bit")
     assert bad == 0
     g = float(to_np(gamma)[0])

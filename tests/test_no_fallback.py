@@ -45,3 +45,28 @@ def test_package_never_imports_the_oracle():
             else:
                 continue
             assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), (name, mods)
+
+
+def test_binding_refuses_a_stale_library(tmp_path):
+    """The library records a digest of the sources it was built from; a copy
+    of the package whose kernel sources differ from the built library's
+    refuses to import instead of running (and timing) the old code."""
+    pkg = tmp_path / "ternary_weight_linear_bitlinear_amd"
+    shutil.copytree(PKG, pkg, ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    code = ("import sys\n"
+            "try:\n"
+            "    import ternary_weight_linear_bitlinear_amd.bitlinear\n"
+            "except ImportError as e:\n"
+            "    print('refused:', e)\n"
+            "    sys.exit(4)\n"
+            "print('loaded')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "loaded" in r.stdout, r.stdout + r.stderr
+    with open(pkg / "csrc" / "gemm.hip", "a") as f:
+        f.write("\n// an edit after the build\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 4, r.stdout + r.stderr
+    assert "built from other sources" in r.stdout
