@@ -7,7 +7,9 @@ token, W 4096 x 4096 bf16 quantised once, x bf16 N(0,1) with 1% outliers at
 +/-20). One step = one token through one layer: per-token INT8 quantisation
 of x, then the integer product with the fused dequant epilogue. Steps rotate
 over 128 distinct packed weight copies (512 MiB, twice the 256 MB
-Infinity Cache) so the weights come from HBM.
+Infinity Cache), and the caches are flushed (a 512 MiB read) right before
+every timed replay, so every timed launch reads its weights from HBM whatever
+the step count.
 
 The same run measures the other rows of the path and reports them under
 "rows": the base-3 layout of the decode GEMV, weight packing, activation
@@ -21,9 +23,13 @@ bf16 weights through torch linear (hipBLASLt).
 Timing: every measured sequence is captured once into a HIP graph and
 replayed between two HIP events on the replay stream, so host-side launch
 cost is not measured. `roofline` describes the dominant kernel (the 2-bit
-decode GEMV): algorithmic bytes per launch over its mean launch duration,
-from a graph of 256 back-to-back launches over rotating weight copies. `cpu_baseline` times the CPU oracle on
-a bounded sample of the same decode workload.
+fused decode step): algorithmic bytes per launch over its mean launch
+duration in the timed graph, against the 8 TB/s datasheet peak and against
+a measured ceiling, a plain streaming read of one 4 MiB buffer per launch
+over the same rotation (rows.ceilings also holds a 512 MiB read, the graph
+cadence of empty launches and an INT8 matrix-core loop). `cpu_baseline`
+times the CPU oracle on a bounded sample of the same decode workload, plus
+each stage of the pass on one thread and on all host threads.
 """
 from __future__ import annotations
 
@@ -50,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=128, help="distinct packed weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default="", help="comma list of rows to run (profiling runs)")
     ap.add_argument("--mode", default="full", choices=["full", "profile"],
                     help="profile: only the fused decode kernel (64 launches over rotating "
@@ -90,11 +96,39 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    # probes: a plain streaming read (also the cache flush), empty launches
+    # and an INT8 matrix-core loop
+    import ctypes
+    if not os.path.exists(_build.PROBES_PATH):
+        _build.build_probes()
+    probes = ctypes.CDLL(_build.PROBES_PATH)
+    probes.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    probes.probe_empty.argtypes = [ctypes.c_void_p]
+    probes.probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe_out = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+
+    def cur_stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def probe_read(buf, blocks, unroll):
+        st = probes.probe_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                               blocks, unroll, ctypes.c_void_p(probe_out.data_ptr()), cur_stream())
+        assert st == 0, f"probe_read: HIP error {st}"
+
+    # 512 MiB read before every timed replay: evicts the 256 MB Infinity Cache
+    # and the L2s, so timed launches find nothing of earlier replays in them
+    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        probe_read(flush_buf, 2048, 4)
+
     def graph_ms(fn, n, warm=3, warm_ms=25.0):
         """Capture fn(0..n-1) into one HIP graph; replay it untimed at least `warm`
-        times and for at least `warm_ms` of GPU time (clocks and caches reach steady
-        state: heavy GEMMs run ~10% slower in the first tens of milliseconds), then
-        once between two HIP events on the replay stream. Returns ms per call."""
+        times and for at least `warm_ms` of GPU time (clocks reach steady state:
+        heavy GEMMs run ~10% slower in the first tens of milliseconds), flush the
+        caches, then replay once between two HIP events on the replay stream.
+        Returns ms per call."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -115,6 +149,7 @@ def main():
             torch.cuda.synchronize()
             spent += a.elapsed_time(b)
             reps += 1
+        flush()
         torch.cuda.synchronize()
         a.record()
         g.replay()
@@ -221,6 +256,50 @@ def main():
         torch.cuda.empty_cache()
     rows["decode_gemv"] = decode
 
+    # ------------------------------------------------------------- ceilings
+    # What the machine at hand reaches on the simplest kernels of each kind:
+    # a streaming read of one 4 MiB buffer per launch (the decode layer's
+    # weight bytes) over 128 rotating buffers, caches flushed; the same read
+    # over 512 MiB in one launch; the graph cadence of empty launches; and
+    # independent v_mfma_i32_32x32x32_i8 chains on register operands (dense
+    # INT8 rate at the clock held under load). The read takes the best of a
+    # few launch shapes.
+    ceil = {}
+    bufs = [torch.randint(0, 256, (4 << 20,), dtype=torch.uint8, device=dev) for _ in range(R)]
+    best = None
+    for blocks, unroll in ((256, 4), (512, 2), (1024, 1), (128, 8), (256, 2), (512, 4)):
+        ms = graph_ms(lambda i, b=blocks, u=unroll: probe_read(bufs[i % R], b, u), R)
+        if best is None or ms < best[0]:
+            best = (ms, blocks, unroll)
+    ceil["stream_read_4MiB"] = dict(ms=best[0], gbs=(4 << 20) / (best[0] * 1e-3) / 1e9,
+                                    blocks=best[1], loads_in_flight=best[2],
+                                    what="one 4 MiB buffer per launch, 128 rotating, cold caches")
+    del bufs
+    big = torch.randint(0, 256, (512 << 20,), dtype=torch.uint8, device=dev)
+    best = None
+    for blocks, unroll in ((2048, 4), (4096, 2), (1024, 8), (8192, 1)):
+        ms = graph_ms(lambda i, b=blocks, u=unroll: probe_read(big, b, u), 4)
+        if best is None or ms < best[0]:
+            best = (ms, blocks, unroll)
+    ceil["stream_read_512MiB"] = dict(ms=best[0], gbs=(512 << 20) / (best[0] * 1e-3) / 1e9,
+                                      blocks=best[1], loads_in_flight=best[2])
+    del big
+    ms = graph_ms(lambda i: probes.probe_empty(cur_stream()), 256)
+    ceil["empty_launch_graph_us"] = ms * 1e3
+    mf_blocks, mf_iters = 1024, 8000
+    ms = graph_ms(lambda i: probes.probe_mfma_i8(mf_blocks, mf_iters,
+                                                 ctypes.c_void_p(probe_out.data_ptr()),
+                                                 cur_stream()), 1)
+    mops = mf_blocks * 4 * mf_iters * 8 * 65536.0
+    ceil["mfma_i8_loop"] = dict(ms=ms, tops=mops / (ms * 1e-3) / 1e12,
+                                frac_of_peak=mops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS)
+    rows["ceilings"] = ceil
+    log(f"ceilings: 4 MiB read {ceil['stream_read_4MiB']['ms']*1e3:.2f} us "
+        f"({ceil['stream_read_4MiB']['gbs']:.0f} GB/s), 512 MiB read "
+        f"{ceil['stream_read_512MiB']['gbs']:.0f} GB/s, empty launch "
+        f"{ceil['empty_launch_graph_us']:.2f} us, INT8 MFMA loop {ceil['mfma_i8_loop']['tops']:.0f} TOPS")
+    torch.cuda.empty_cache()
+
     # Weight streaming at a size where launch latency no longer dominates:
     # one token against a 32768 x 4096 ternary matrix (32 MiB packed, the
     # shape of a vocabulary projection), 16 rotating copies.
@@ -280,7 +359,9 @@ def main():
                 xq, sc, packed, gamma, q.N, q.K, layout, torch.bfloat16, y=y)
             ms = graph_ms(f, 10)
             pre[layout] = dict(gemm_ms=ms, tops=ops / (ms * 1e-3) / 1e12,
-                               frac=ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS)
+                               frac=ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                               frac_of_measured_mfma=ops / (ms * 1e-3) / 1e12 /
+                               rows["ceilings"]["mfma_i8_loop"]["tops"])
             log(f"prefill {layout}: {ms*1e3:.1f} us = {pre[layout]['tops']:.0f} TOPS")
         rows["prefill_gemm"] = pre
         del Wp, xp, xq, sc
@@ -447,6 +528,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
+        nthreads = oracle.num_threads()  # all host threads (OpenMP default)
         codes, _, gamma = oracle.ternary_codes(p.w)
         n = 0
         t0 = time.perf_counter()
@@ -459,12 +541,46 @@ def main():
                 break
         dt = time.perf_counter() - t0
         wb = decode["2bit"]["weight_bytes"]
-        cpu = {"value": wb * n / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+
+        def median_ms(f, reps=3):
+            ts = []
+            for _ in range(reps):
+                t1 = time.perf_counter()
+                f()
+                ts.append((time.perf_counter() - t1) * 1e3)
+            return sorted(ts)[len(ts) // 2]
+
+        def stages(prob):
+            """Median of 3 runs of each stage of the pass on this problem."""
+            g32 = oracle.absmean(prob.w)[0]
+            cds = oracle.ternary_codes(prob.w)[0]
+            xq1, s1, _ = oracle.quant_acts(prob.x)
+            acc1 = oracle.int_product(xq1, cds)
+            return {"absmean_ms": median_ms(lambda: oracle.absmean(prob.w)),
+                    "ternarise_ms": median_ms(lambda: oracle.ternary_codes(prob.w, gamma=g32)),
+                    "pack_2bit_ms": median_ms(lambda: oracle.pack(cds, "2bit")),
+                    "quant_acts_ms": median_ms(lambda: oracle.quant_acts(prob.x)),
+                    "int_product_ms": median_ms(lambda: oracle.int_product(xq1, cds)),
+                    "epilogue_ms": median_ms(lambda: oracle.epilogue(acc1, g32, s1))}
+
+        per_stage = {}
+        tiny = synth.workload("tiny")
+        for label, prob in (("tiny_M8_N256_K256_f32", tiny), ("decode_M1_N4096_K4096_bf16", p)):
+            per_stage[label] = {}
+            for th in (1, nthreads):
+                oracle.set_num_threads(th)
+                per_stage[label][f"threads_{th}"] = stages(prob)
+        oracle.set_num_threads(nthreads)
+        cpu = {"value": wb * n / dt / 1e9, "unit": "GB/s", "cores": nthreads,
                "kind": "oracle",
                "sample": f"{n} decode steps (quant_acts + int64 product + fp64 epilogue, M=1, "
-                         f"K=N=4096) in {dt:.1f} s; value = 2-bit weight bytes per step / time",
-               "host_cpus": os.cpu_count()}
-        log(f"cpu baseline: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+                         f"K=N=4096) in {dt:.1f} s on {nthreads} threads; value = 2-bit weight "
+                         "bytes per step / time. stages: each stage of the pass (median of 3) on "
+                         "1 thread and on all threads, for the tiny and decode workloads",
+               "host_cpus": os.cpu_count(),
+               "stages": per_stage}
+        log(f"cpu baseline: {cpu['value']:.3f} GB/s on {cpu['cores']} threads; decode stages "
+            f"1 thread: {per_stage['decode_M1_N4096_K4096_bf16']['threads_1']}")
 
     # ------------------------------------------------------------ roofline
     d2 = decode["2bit"]
@@ -472,7 +588,12 @@ def main():
             "bound": "hbm", "achieved": d2["fused_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": d2["fused_gbs"] / HBM_PEAK_GBS, "traffic": None,
             "alg_bytes_per_launch": d2["fused_alg_bytes"],
-            "launch_ms_mean": d2["ms_per_step"]}
+            "launch_ms_mean": d2["ms_per_step"],
+            "measured_ceiling": {
+                "what": "plain streaming read of one 4 MiB buffer per launch, 128 rotating "
+                        "buffers, caches flushed (rows.ceilings.stream_read_4MiB)",
+                "gbs": rows["ceilings"]["stream_read_4MiB"]["gbs"],
+                "frac": d2["fused_gbs"] / rows["ceilings"]["stream_read_4MiB"]["gbs"]}}
     counters = os.path.join(ROOT, "profiles", "decode_fused_2bit_counters.json")
     if os.path.exists(counters):
         with open(counters) as f:
@@ -493,7 +614,8 @@ def main():
         "config": {"workload": "decode GEMV: M=1 token, W 4096x4096 bf16 ~N(0,0.02) quantised "
                                "once (absmean ternary, 2-bit packed), x bf16 ~N(0,1) + 1% +/-20 "
                                "outliers; step = per-token INT8 quantisation + integer product + "
-                               "dequant (one fused launch); 128 rotating weight copies",
+                               "dequant (one fused launch); 128 rotating weight copies "
+                               "(512 MiB), caches flushed before the timed replay",
                    "M": 1, "K": 4096, "N": 4096, "layout": "2bit", "out": "fp32"},
         "roofline": roof,
         "cpu_baseline": cpu,
