@@ -121,6 +121,27 @@ bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t 
                                  void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* Allocation-free variant of bitlinear_pack_weights, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same quantisation and packing, with
+ * the same arguments and results, but the mean's partial sums live in the
+ * library's own scratch array of bitlinear_pack_noalloc_max_scratch_bytes()
+ * bytes (16 KiB), held by every GPU the library runs on until the process
+ * ends, instead of in a caller workspace. Nothing is allocated or freed, by
+ * the library or by any routine it calls. Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (concurrent streams, threads
+ * or graph replays) race and may produce wrong scales; serialise them. Each
+ * call rewrites every partial it reads, so nothing needs clearing between
+ * calls. Shapes whose partial sums would not fit return BL_ERR_INVALID_ARG
+ * (the mean uses at most 1024 partials, so every accepted shape fits); a
+ * failed look-up of the scratch's device address returns BL_ERR_DEVICE. */
+bl_status bitlinear_pack_weights_noalloc(const void *W, int w_dtype, int64_t N, int64_t K,
+                                         int scheme, int layout, float eps,
+                                         uint8_t *packed, float *gamma, void *stream);
+
+/* Bytes of the allocation-free pack's scratch array (per GPU). Host-only. */
+size_t bitlinear_pack_noalloc_max_scratch_bytes(void);
+
 /* Per-token symmetric absmax INT8 quantisation ([b158] §3.2 and §5.2):
  * s_m = max(max_k |x[m,k]|, 1e-6); xq = clamp(round(x / s_m * 127), -127, 127)
  * with fp32 division, then * 127, then round half to even.

@@ -61,6 +61,10 @@ _lib.bitlinear_pack_workspace_bytes.restype = _sz
 _lib.bitlinear_pack_workspace_bytes.argtypes = [_i64, _i64]
 _lib.bitlinear_pack_weights.restype = _int
 _lib.bitlinear_pack_weights.argtypes = [_p, _int, _i64, _i64, _int, _int, _f32, _p, _p, _p, _sz, _p]
+_lib.bitlinear_pack_weights_noalloc.restype = _int
+_lib.bitlinear_pack_weights_noalloc.argtypes = [_p, _int, _i64, _i64, _int, _int, _f32, _p, _p, _p]
+_lib.bitlinear_pack_noalloc_max_scratch_bytes.restype = _sz
+_lib.bitlinear_pack_noalloc_max_scratch_bytes.argtypes = []
 _lib.bitlinear_quant_acts.restype = _int
 _lib.bitlinear_quant_acts.argtypes = [_p, _int, _i64, _i64, _p, _p, _p]
 _lib.bitlinear_forward.restype = _int
@@ -87,7 +91,8 @@ _lib.bitlinear_version.restype = _int
 _lib.bitlinear_version.argtypes = []
 
 EXPORTED = ["bitlinear_packed_row_bytes", "bitlinear_pack_workspace_bytes",
-            "bitlinear_pack_weights", "bitlinear_quant_acts", "bitlinear_forward",
+            "bitlinear_pack_weights", "bitlinear_pack_weights_noalloc",
+            "bitlinear_pack_noalloc_max_scratch_bytes", "bitlinear_quant_acts", "bitlinear_forward",
             "bitlinear_linear", "bitlinear_forward_segmented", "bitlinear_linear_segmented",
             "bitlinear_forward_lut", "bitlinear_backward_input", "bitlinear_backward_weight",
             "bitlinear_forward_plan", "bitlinear_status_string", "bitlinear_version",
@@ -180,6 +185,24 @@ def bitlinear_pack_weights(W: torch.Tensor, layout="2bit", scheme="ternary", eps
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
            "bitlinear_pack_weights")
     return packed, gamma
+
+
+def bitlinear_pack_weights_noalloc(W: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor,
+                                   layout="2bit", scheme="ternary", eps: float = 1e-5,
+                                   stream=None):
+    """bitlinear_pack_weights into caller-provided packed / gamma, with the
+    library's own scratch instead of a workspace (nothing is allocated)."""
+    assert W.dim() == 2 and W.is_contiguous() and W.dtype in _DTYPES
+    N, K = W.shape
+    _check(_lib.bitlinear_pack_weights_noalloc(
+        _ptr(W), _DTYPES[W.dtype], N, K, SCHEMES[scheme] if isinstance(scheme, str) else int(scheme),
+        _layout(layout), float(eps), _ptr(packed), _ptr(gamma), _stream(stream)),
+        "bitlinear_pack_weights_noalloc")
+    return packed, gamma
+
+
+def bitlinear_pack_noalloc_max_scratch_bytes() -> int:
+    return int(_lib.bitlinear_pack_noalloc_max_scratch_bytes())
 
 
 def bitlinear_quant_acts(x: torch.Tensor, xq: torch.Tensor | None = None,

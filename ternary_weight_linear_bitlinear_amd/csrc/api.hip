@@ -153,6 +153,34 @@ bl_status bitlinear_pack_weights(const void *W, int w_dtype, int64_t N, int64_t 
                                     static_cast<hipStream_t>(stream)));
 }
 
+bl_status bitlinear_pack_weights_noalloc(const void *W, int w_dtype, int64_t N, int64_t K,
+                                         int scheme, int layout, float eps, uint8_t *packed,
+                                         float *gamma, void *stream) {
+    if (!W || !packed || !gamma) return BL_ERR_INVALID_ARG;
+    if (!aligned16(W) || !aligned16(packed) || !aligned4(gamma)) return BL_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || K > kMaxK) return BL_ERR_INVALID_ARG;
+    if (N > INT64_MAX / K) return BL_ERR_INVALID_ARG;
+    if (!valid_dtype(w_dtype) || !valid_layout(layout) || !valid_scheme(scheme))
+        return BL_ERR_INVALID_ARG;
+    if (layout == BL_PACK_1BIT && scheme != BL_BINARY) return BL_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f) return BL_ERR_INVALID_ARG;
+    if (bl::pack_workspace_bytes(N * K) > bitlinear_pack_noalloc_max_scratch_bytes())
+        return BL_ERR_INVALID_ARG;
+    bl_status st = device_ok();
+    if (st != BL_OK) return st;
+    double *scratch = nullptr;
+    size_t scratch_bytes = 0;
+    if (bl::pack_scratch(&scratch, &scratch_bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return BL_ERR_DEVICE;
+    }
+    if (bl::pack_workspace_bytes(N * K) > scratch_bytes) return BL_ERR_INVALID_ARG;
+    return launched(bl::launch_pack(W, w_dtype, N, K, scheme, layout, eps, packed, gamma,
+                                    scratch, static_cast<hipStream_t>(stream)));
+}
+
+size_t bitlinear_pack_noalloc_max_scratch_bytes(void) { return bl::pack_scratch_capacity(); }
+
 bl_status bitlinear_quant_acts(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *xq,
                                float *scale, void *stream) {
     if (!x || !xq || !scale) return BL_ERR_INVALID_ARG;

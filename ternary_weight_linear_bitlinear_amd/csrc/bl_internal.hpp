@@ -141,6 +141,10 @@ hipError_t launch_pack(const void *W, int dtype, int64_t N, int64_t K, int schem
                        double *workspace, hipStream_t stream);
 hipError_t launch_quant_acts(const void *x, int dtype, int64_t M, int64_t K,
                              int8_t *xq, float *scale, hipStream_t stream);
+// Device address and size of the library's own pack scratch on the current
+// device (looked up on the first call per device).
+hipError_t pack_scratch(double **ptr, size_t *bytes);
+size_t pack_scratch_capacity();  // bytes of that scratch (host-only, no device needed)
 
 // ---- products (skinny.hip, gemm.hip) -------------------------------------
 // Whether the weight-streaming kernel (in 16-token chunks) or the tiled GEMM

@@ -380,6 +380,36 @@ hipError_t pack_t(const T *w, int64_t N, int64_t K, int scheme, int layout, floa
 
 }  // namespace
 
+// Scratch of the allocation-free pack (bitlinear_pack_weights_noalloc): the
+// mean's per-block partial sums, at most kMaxParts pairs of doubles (16 KiB),
+// in a file-scope device array that every GPU the library runs on holds until
+// the process ends. Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol): each device's address is
+// looked up once, with that device current, and kept here.
+static __device__ __align__(256) double2 scratch[kMaxParts];
+static std::atomic<double2 *> g_scratch_addr[64];
+
+hipError_t pack_scratch(double **ptr, size_t *bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    double2 *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (addr == nullptr) return hipErrorInvalidSymbol;
+        p = static_cast<double2 *>(addr);
+        g_scratch_addr[dev].store(p, std::memory_order_release);  // same value if two race
+    }
+    *ptr = reinterpret_cast<double *>(p);
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
+
+size_t pack_scratch_capacity() { return sizeof(scratch); }
+
 int absmean_parts(int64_t count) {
     const int64_t per = (int64_t)kThreads * 8 * 4;  // one unrolled sweep per block
     const int64_t p = (count + per - 1) / per;

@@ -252,3 +252,31 @@ def test_forward_plan_never_launches_an_empty_grid(bl, layout, M, N):
     for line in plan:
         gx = int(line.split("grid=")[1].split("x")[0])
         assert gx > 0, line
+
+
+def test_noalloc_pack_rejects(bl):
+    """The allocation-free pack validates like the workspace pack, before any
+    device call."""
+    lib = bl.library()
+    args = dict(W=P, w_dtype=1, N=8, K=64, scheme=0, layout=0, eps=1e-5, packed=P, gamma=P)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.bitlinear_pack_weights_noalloc(
+            a["W"], a["w_dtype"], a["N"], a["K"], a["scheme"], a["layout"], a["eps"], a["packed"],
+            a["gamma"], None)
+
+    assert call(W=None) == bl.BL_ERR_INVALID_ARG
+    assert call(packed=P + 8) == bl.BL_ERR_INVALID_ARG
+    assert call(N=0) == bl.BL_ERR_INVALID_ARG
+    assert call(K=16909321) == bl.BL_ERR_INVALID_ARG
+    assert call(layout=2, scheme=0) == bl.BL_ERR_INVALID_ARG  # 1-bit holds binary codes only
+    assert call(eps=float("nan")) == bl.BL_ERR_INVALID_ARG
+    assert call(w_dtype=5) == bl.BL_ERR_INVALID_ARG
+    assert bl.bitlinear_pack_noalloc_max_scratch_bytes() == 16384
+    # the largest shape still fits: the mean never uses more than 1024 partials
+    assert bl.bitlinear_pack_workspace_bytes(1 << 20, 1 << 20) <= 16384
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == bl.BL_ERR_DEVICE  # valid arguments, no gfx950 device
