@@ -63,6 +63,7 @@ constexpr int64_t kSkinnyMaxM = 16;
 // the attribute twice is harmless, so two threads racing here only repeat
 // the call. A request above the free space is refused here instead of
 // failing at launch.
+constexpr size_t kLdsBytesPerCu = 160 * 1024;
 using LdsFlag = std::atomic<uint64_t>;
 template <typename F>
 hipError_t allow_dynamic_lds(F *kernel, size_t bytes, LdsFlag *done) {
@@ -72,7 +73,7 @@ hipError_t allow_dynamic_lds(F *kernel, size_t bytes, LdsFlag *done) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
     if (bit != 0 && (done->load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
-    constexpr size_t kLdsBytes = 160 * 1024;
+    constexpr size_t kLdsBytes = kLdsBytesPerCu;
     hipFuncAttributes attr{};
     e = hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel));
     if (e != hipSuccess) return e;

@@ -95,6 +95,17 @@ __device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x
 // The memory clobber keeps the compiler from moving memory accesses across it.
 // Only for barriers whose purpose is LDS reuse; global memory written before
 // it is not made visible to other waves.
+// Immediate of s_waitcnt that waits until at most n vector-memory operations
+// of this wave are outstanding (n < 64) and leaves the other counters alone
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// A generic pointer into LDS as the LDS-address-space pointer that
+// direct-to-LDS loads take.
+__device__ __forceinline__ __attribute__((address_space(3))) void *to_lds(void *p) {
+    return (__attribute__((address_space(3))) void *)p;
+}
+
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

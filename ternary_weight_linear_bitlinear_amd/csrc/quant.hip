@@ -263,6 +263,33 @@ __device__ __forceinline__ float block_max(float v) {
     return r;
 }
 
+// Eight consecutive elements as loaded (one 16-byte piece of bf16, two of
+// fp32), widened to fp32 only after every load of the thread is in flight.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    uint4 a;
+    __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void widen(float v[8]) const {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void widen(float v[8]) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
 template <typename T, int J>
 __global__ __launch_bounds__(kThreads) void quant_acts_kernel(
     const T *__restrict__ x, int64_t M, int64_t K, int8_t *__restrict__ xq,
@@ -275,24 +302,36 @@ __global__ __launch_bounds__(kThreads) void quant_acts_kernel(
     float amax = 0.f;
     if (J > 0) {
         float v[J > 0 ? J : 1][8];
+        if (vec) {
+            // every load first (chunks past the row re-read its last chunk and
+            // are zeroed below), so the J loads overlap instead of each
+            // waiting for the one before
+            Raw8<T> raw[J > 0 ? J : 1];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int64_t c = threadIdx.x + (int64_t)j * kThreads;
-            if (c < nchunk) {
-                if (vec) {
-                    load8(row + c * 8, v[j]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v[j][e] = c * 8 + e < K ? Elem<T>::get(row, c * 8 + e) : 0.f;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+            for (int j = 0; j < J; ++j) {
+                const int64_t c = threadIdx.x + (int64_t)j * kThreads;
+                raw[j].load(row + (c < nchunk ? c : nchunk - 1) * 8);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+            for (int j = 0; j < J; ++j) {
+                const int64_t c = threadIdx.x + (int64_t)j * kThreads;
+                raw[j].widen(v[j]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[j][e] = c < nchunk ? v[j][e] : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int64_t c = threadIdx.x + (int64_t)j * kThreads;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[j][e] = c < nchunk && c * 8 + e < K ? Elem<T>::get(row, c * 8 + e) : 0.f;
+            }
         }
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
         const float s = fmaxf(block_max(amax), 1e-6f);
         const float y = 1.0f / s;
         if (threadIdx.x == 0) scale[m] = s;

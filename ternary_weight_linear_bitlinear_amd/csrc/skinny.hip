@@ -28,8 +28,9 @@ namespace {
 // per CU (shorter serial expand/multiply chain per wave once the data lands;
 // long rows). From kWideN rows on (at least four workgroups per CU) four waves
 // with four loads keep more bytes in flight per CU and stream faster.
-// Batches at N >= 8192 put two row groups in a workgroup, halving the
-// activation staging per weight byte.
+// Batches at N >= 8192 put three (up to 12288 rows: one round of at most
+// 256 workgroups) or two row groups in a workgroup, cutting the activation
+// staging per weight byte.
 constexpr int kSkKS = 8, kSkNSS = 2, kSkRG2MinN = 8192;
 constexpr int kFdKS = 8, kFdNSS = 2;
 constexpr int64_t kWideN = 16384;
@@ -105,6 +106,22 @@ __device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut,
     }
 }
 
+// The activation operands of one unit's matrix-core steps (16 bytes each, one
+// token row of the staged tile), read back to back so that their LDS
+// latencies overlap.
+//
+// Both decode kernels feed the matrix cores without masking. Lanes of tokens
+// past M read token M - 1's row (`tok` below), so their output columns hold
+// copies that are never stored. Weight loads that fall outside the matrix
+// (rows past N, units past the row) read a valid address and are not zeroed:
+// rows past N only reach outputs that are never stored, and units past the
+// row meet activations that are staged as zero past K, so they add nothing.
+template <int STEPS>
+__device__ __forceinline__ void read_act_unit(const int8_t *p, v4i (&b)[STEPS]) {
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) b[st] = *reinterpret_cast<const v4i *>(p + 16 * st);
+}
+
 // Epilogue of the decode products: four consecutive outputs n .. n + 3 of one
 // token (row pointers yt, acct) from their INT32 sums, y = acc * gamma *
 // scale / 127. A single matrix takes one factor; stacked segments pick each
@@ -147,7 +164,9 @@ __device__ __forceinline__ void store_outputs(const GammaMap &gm,
 // into registers first, then the weight loads are issued. Vector-memory
 // counters complete in issue order, so the wait for the activations leaves
 // every weight load in flight, and the LDS staging overlaps the HBM latency.
-template <int LAYOUT, int KS, int NSS, int RG, int MAXM, typename YT>
+// MR: rows longer than one round (a separate instantiation, so one-round rows
+// keep the registers the next round's requests would take).
+template <int LAYOUT, int KS, int NSS, int RG, int MAXM, bool MR, typename YT>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ scale,
     const uint8_t *__restrict__ packed, const GammaMap gm, int M, int64_t N,
@@ -202,85 +221,136 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
         wrow[q] = packed + (n0 + 16 * q + r) * rb;
     }
 
+    const int tok = r < M ? r : M - 1;  // token row this lane's activation operand reads
     v4i acc[RG];
 #pragma unroll
     for (int q = 0; q < RG; ++q) acc[q] = v4i{0, 0, 0, 0};
-    for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
-        const int64_t k0 = u0 * C::kUnitCodes;
-        // 1. this thread's chunks of xq[0:M, k0 : k0 + kRoundK] (16 bytes each;
-        //    with K % 16 == 0 a chunk is entirely inside or outside the row)
-        //    Out-of-range pieces (activations and weights alike) load a valid
-        //    address unconditionally and are zeroed where they are consumed: a
-        //    select right at the load would make the compiler wait for it there.
-        v4i xa[kMaxQ];
-        bool xok[kMaxQ];
-        if (aligned) {
-#pragma unroll
-            for (int i = 0; i < kMaxQ; ++i) {
-                const int q = threadIdx.x + i * kThreads;
-                const int t = q / kChunksPerTok;
-                const int64_t k = k0 + (q % kChunksPerTok) * 16;
-                xok[i] = q < chunks && k < K;
-                xa[i] = *reinterpret_cast<const v4i *>(xok[i] ? xq + (int64_t)t * K + k : xq);
-            }
-        }
-        // 2. every weight load of this round
-        uint4 wv[RG][NSS];
-        bool wok[RG][NSS];
+
+    // every weight load of the round starting at unit u0. Out-of-range units
+    // load a valid address and are used as loaded (see read_act_unit): a
+    // select right at the load would make the compiler wait for it there.
+    uint4 wv[RG][NSS];
+    auto issue_w = [&](int64_t u0) {
 #pragma unroll
         for (int q = 0; q < RG; ++q)
 #pragma unroll
             for (int s = 0; s < NSS; ++s) {
                 const int64_t unit = u0 + (int64_t)(s * KS + wave) * 4 + g;
-                wok[q][s] = row_ok[q] && unit < units;
-                wv[q][s] = load_unit<LAYOUT>(wok[q][s] ? wrow[q] + unit * C::kUnitBytes : packed);
+                const bool ok = row_ok[q] && unit < units;
+                wv[q][s] = load_unit<LAYOUT>(ok ? wrow[q] + unit * C::kUnitBytes : packed);
             }
-        // 3. stage the activations in LDS (zero past K)
-        lds_barrier();  // previous round's readers are done
-        if (aligned) {
-#pragma unroll
-            for (int i = 0; i < kMaxQ; ++i) {
-                const int q = threadIdx.x + i * kThreads;
-                if (q < chunks)
-                    *reinterpret_cast<v4i *>(act + (q / kChunksPerTok) * kActStride +
-                                             (q % kChunksPerTok) * 16) =
-                        xok[i] ? xa[i] : v4i{0, 0, 0, 0};
-            }
-        } else {
-            for (int q = threadIdx.x; q < chunks; q += kThreads) {
-                const int t = q / kChunksPerTok, cc = q % kChunksPerTok;
-                const int64_t k = k0 + cc * 16;
-                const int8_t *src = xq + (int64_t)t * K;
-                uint32_t d[4] = {0u, 0u, 0u, 0u};
-                for (int e = 0; e < 16; ++e)
-                    if (k + e < K) d[e / 4] |= (uint32_t)(uint8_t)src[k + e] << (8 * (e % 4));
-                *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) =
-                    v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
-            }
+    };
+    // chunks of K % 16 != 0 rows, byte by byte (zero past K)
+    auto stage_bytes = [&](int64_t k0) {
+        for (int q = threadIdx.x; q < chunks; q += kThreads) {
+            const int t = q / kChunksPerTok, cc = q % kChunksPerTok;
+            const int64_t k = k0 + cc * 16;
+            const int8_t *src = xq + (int64_t)t * K;
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 16; ++e)
+                if (k + e < K) d[e / 4] |= (uint32_t)(uint8_t)src[k + e] << (8 * (e % 4));
+            *reinterpret_cast<v4i *>(act + t * kActStride + cc * 16) =
+                v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
         }
-        lds_barrier();
-        // 4. expand and multiply; one activation read feeds RG instructions
+    };
+    // expand and multiply one round; one activation read feeds RG instructions
+    auto multiply = [&]() {
+        v4i b[NSS][C::kSteps];
+#pragma unroll
+        for (int s = 0; s < NSS; ++s)
+            read_act_unit<C::kSteps>(
+                act + tok * kActStride + ((s * KS + wave) * 4 + g) * C::kUnitCodes, b[s]);
 #pragma unroll
         for (int s = 0; s < NSS; ++s) {
             int c[RG][20];
 #pragma unroll
-            for (int q = 0; q < RG; ++q)
-                decode_unit<LAYOUT>(wok[q][s] ? wv[q][s] : make_uint4(0u, 0u, 0u, 0u), lut,
-                                    c[q]);
-            const int ul = (s * KS + wave) * 4 + g;  // unit within the round
+            for (int q = 0; q < RG; ++q) decode_unit<LAYOUT>(wv[q][s], lut, c[q]);
 #pragma unroll
             for (int st = 0; st < C::kSteps; ++st) {
-                v4i b = {0, 0, 0, 0};
-                if (r < M)
-                    b = *reinterpret_cast<const v4i *>(act + r * kActStride +
-                                                       ul * C::kUnitCodes + 16 * st);
 #pragma unroll
                 for (int q = 0; q < RG; ++q) {
                     const v4i a = {c[q][4 * st], c[q][4 * st + 1], c[q][4 * st + 2],
                                    c[q][4 * st + 3]};
-                    acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[q], 0, 0, 0);
+                    acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[s][st], acc[q], 0, 0, 0);
                 }
             }
+        }
+    };
+
+    if constexpr (!MR) {
+        // One round: this thread's chunks of xq[0:M, 0:K] (16 bytes each; with
+        // K % 16 == 0 a chunk is entirely inside or outside the row) go
+        // straight into LDS (16-byte direct-to-LDS loads, no registers) ahead
+        // of the weights: vector-memory counters complete in issue order, so
+        // the wait for them leaves every weight load in flight. A wave's 64
+        // chunks are consecutive in one token row (64 divides the chunks per
+        // row), so its LDS offset is uniform. Chunks past K read a placeholder
+        // address and are zeroed once they have landed.
+        if (aligned) {
+#pragma unroll
+            for (int i = 0; i < kMaxQ; ++i) {
+                const int qw = __builtin_amdgcn_readfirstlane(threadIdx.x - lane + i * kThreads);
+                const int t = qw / kChunksPerTok;
+                if (t < M) {  // wave-uniform
+                    const int64_t k = (qw % kChunksPerTok + lane) * 16;
+                    const int8_t *src = k < K ? xq + (int64_t)t * K + k : xq;
+                    __builtin_amdgcn_global_load_lds(
+                        src, to_lds(act + t * kActStride + (qw % kChunksPerTok) * 16), 16, 0, 0);
+                }
+            }
+        }
+        issue_w(0);
+        if (aligned) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(RG * NSS));
+            if (kRoundK > K) {
+#pragma unroll
+                for (int i = 0; i < kMaxQ; ++i) {
+                    const int q = threadIdx.x + i * kThreads;
+                    const int64_t k = (q % kChunksPerTok) * 16;
+                    if (q < chunks && k >= K)
+                        *reinterpret_cast<v4i *>(act + (q / kChunksPerTok) * kActStride +
+                                                 (q % kChunksPerTok) * 16) = v4i{0, 0, 0, 0};
+                }
+            }
+        } else {
+            stage_bytes(0);
+        }
+        lds_barrier();
+        multiply();
+    } else {
+        // Several rounds: each round's activation chunks are loaded into
+        // registers ahead of its weights, before the barrier that lets the
+        // tile be rewritten, so both overlap the previous round's tail.
+        for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
+            const int64_t k0 = u0 * C::kUnitCodes;
+            v4i xa[kMaxQ];
+            bool xok[kMaxQ];
+            if (aligned) {
+#pragma unroll
+                for (int i = 0; i < kMaxQ; ++i) {
+                    const int q = threadIdx.x + i * kThreads;
+                    const int t = q / kChunksPerTok;
+                    const int64_t k = k0 + (q % kChunksPerTok) * 16;
+                    xok[i] = q < chunks && k < K;
+                    xa[i] = *reinterpret_cast<const v4i *>(xok[i] ? xq + (int64_t)t * K + k : xq);
+                }
+            }
+            issue_w(u0);
+            lds_barrier();  // the previous round's readers are done
+            if (aligned) {
+#pragma unroll
+                for (int i = 0; i < kMaxQ; ++i) {
+                    const int q = threadIdx.x + i * kThreads;
+                    if (q < chunks)
+                        *reinterpret_cast<v4i *>(act + (q / kChunksPerTok) * kActStride +
+                                                 (q % kChunksPerTok) * 16) =
+                            xok[i] ? xa[i] : v4i{0, 0, 0, 0};
+                }
+            } else {
+                stage_bytes(k0);
+            }
+            lds_barrier();
+            multiply();
         }
     }
 
@@ -308,23 +378,29 @@ hipError_t launch_skinny_t(const int8_t *xq, const float *scale, const uint8_t *
     const int64_t rb = row_bytes_of(LAYOUT, K);
     // the partial-tile buffer aliases the activation area (needs KS*RG KiB)
     const int64_t chunk_m = M < MAXM ? M : MAXM;
+    const int64_t round_units = (int64_t)KS * NSS * 4;
+    const size_t lut = LAYOUT == kLayoutBase3 ? 8192 : 0;
     const size_t act = (size_t)chunk_m * (KS * NSS * 4 * SkinnyCfg<LAYOUT>::kUnitCodes + 16);
     const size_t part = (size_t)KS * RG * 1024;
-    const size_t smem = (LAYOUT == kLayoutBase3 ? 8192 : 0) + (act > part ? act : part);
+    const size_t smem = lut + (act > part ? act : part);
     dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)), (unsigned)((M + MAXM - 1) / MAXM)),
         block(64 * KS);
-    auto kern = skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, YT>;
+    const bool mr = rb / SkinnyCfg<LAYOUT>::kUnitBytes > round_units;
     if (t_plan) {
-        plan_note(grid.x, grid.y, block.x, smem, "skinny_kernel<%d, %d, %d, %d, %d, %s>", LAYOUT,
-                  KS, NSS, RG, MAXM, type_name<YT>());
+        plan_note(grid.x, grid.y, block.x, smem, "skinny_kernel<%d, %d, %d, %d, %d, %s, %s>",
+                  LAYOUT, KS, NSS, RG, MAXM, mr ? "true" : "false", type_name<YT>());
         return hipSuccess;
     }
-    static LdsFlag lds_raised{0};  // one flag per instantiation of this launcher
-    hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, block, smem, s, xq, scale, packed, gamma, (int)M, N, K, rb, y,
-                       acc);
-    return hipGetLastError();
+    auto go = [&](auto kern, LdsFlag *flag) {
+        hipError_t e = allow_dynamic_lds(kern, smem, flag);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, grid, block, smem, s, xq, scale, packed, gamma, (int)M, N, K, rb,
+                           y, acc);
+        return hipGetLastError();
+    };
+    static LdsFlag lds_raised[2];  // one flag per kernel of this launcher
+    if (mr) return go(skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, true, YT>, &lds_raised[1]);
+    return go(skinny_kernel<LAYOUT, KS, NSS, RG, MAXM, false, YT>, &lds_raised[0]);
 }
 
 template <int LAYOUT, typename YT>
@@ -338,6 +414,11 @@ hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *
                                                       s);
     if (M <= 4)
         return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 1, 4, YT>(xq, scale, packed, gamma, M, N, K,
+                                                               y, acc, s);
+    // up to 16 x 256 x 3 rows: three row groups, so that one round of
+    // workgroups (at most one per compute unit) covers the matrix
+    if (N >= kSkRG2MinN && N <= 16 * 256 * 3)
+        return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 3, 16, YT>(xq, scale, packed, gamma, M, N, K,
                                                                y, acc, s);
     if (N >= kSkRG2MinN)
         return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 2, 16, YT>(xq, scale, packed, gamma, M, N, K,
@@ -546,6 +627,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         lds_barrier();
     }
 
+    const int tok = r < M ? r : M - 1;  // token row this lane's activation operand reads
     int buf = 0;
     for (int64_t tile = tile0; tile < tiles; tile += gridDim.x) {
         v4i acc[RG];
@@ -569,23 +651,20 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
             }
 #pragma unroll
             for (int s = 0; s < NSS; ++s) {
+                const int ul = (s * KS + wave) * 4 + g;
+                v4i b[C::kSteps];
+                read_act_unit<C::kSteps>(act + tok * kActStride + ul * C::kUnitCodes, b);
                 int c[RG][20];
 #pragma unroll
-                for (int q = 0; q < RG; ++q)
-                    decode_unit<LAYOUT>(wok[q][s] ? wv[q][s] : make_uint4(0u, 0u, 0u, 0u), lut,
-                                        c[q]);
-                const int ul = (s * KS + wave) * 4 + g;
+                for (int q = 0; q < RG; ++q) decode_unit<LAYOUT>(wv[q][s], lut, c[q]);
 #pragma unroll
                 for (int st = 0; st < C::kSteps; ++st) {
-                    v4i b = {0, 0, 0, 0};
-                    if (r < M)
-                        b = *reinterpret_cast<const v4i *>(act + r * kActStride +
-                                                           ul * C::kUnitCodes + 16 * st);
 #pragma unroll
                     for (int q = 0; q < RG; ++q) {
                         const v4i a = {c[q][4 * st], c[q][4 * st + 1], c[q][4 * st + 2],
                                        c[q][4 * st + 3]};
-                        acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[q], 0, 0, 0);
+                        acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[st], acc[q], 0, 0,
+                                                                       0);
                     }
                 }
             }

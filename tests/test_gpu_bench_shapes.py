@@ -169,7 +169,7 @@ def test_bench_decode_two_launch_step(bl, layout):
     p = synth.workload("decode")
     L = {"2bit": 0, "base3": 1, "1bit": 2}[layout]
     check_case(bl, f"decode two-launch {layout}", [p], p, layout, SCHEME[layout], torch.float32,
-               False, f"skinny_kernel<{L}, 8, 2, 1, 4, float>", "256x1")
+               False, f"skinny_kernel<{L}, 8, 2, 1, 4, false, float>", "256x1")
 
 
 @pytest.mark.parametrize("layout", ["2bit", "1bit"])
@@ -201,10 +201,10 @@ def block_inputs(M, K):
 
 
 BLOCK_16 = {
-    "qkv": "skinny_kernel<0, 8, 2, 2, 16, unsigned short>",
-    "o": "skinny_kernel<0, 8, 2, 1, 16, unsigned short>",
-    "up": "skinny_kernel<0, 8, 2, 2, 16, unsigned short>",
-    "down": "skinny_kernel<0, 8, 2, 1, 16, unsigned short>",
+    "qkv": "skinny_kernel<0, 8, 2, 3, 16, false, unsigned short>",
+    "o": "skinny_kernel<0, 8, 2, 1, 16, false, unsigned short>",
+    "up": "skinny_kernel<0, 8, 2, 3, 16, false, unsigned short>",
+    "down": "skinny_kernel<0, 8, 2, 1, 16, true, unsigned short>",
 }
 BLOCK_512 = {
     "qkv": "gemm_kernel<0, 256, 128, 2, 4, 2, 1, 0, unsigned short>",
