@@ -232,11 +232,12 @@ bl_status bitlinear_forward_lut(const int8_t *xq, const float *scale, const uint
  *
  * bitlinear_backward_input: grad_x[m,k] = gamma * sum_n grad_y[m,n] * c[n,k].
  *   grad_y  [M, N] bf16 (gy_dtype must be BL_BF16).
- *   packed  [N, row_bytes] codes in BL_PACK_2BIT (the forward's own matrix; no
- *           transposed copy is needed); gamma: 1 float (device).
+ *   packed  [N, row_bytes] codes in `layout` (BL_PACK_2BIT, BL_PACK_BASE3 or
+ *           BL_PACK_1BIT: the forward's own matrix; no transposed copy is
+ *           needed); gamma: 1 float (device).
  *   grad_x  out: [M, K] fp32.
- * Requires N % 8 == 0. BL_F32 grad_y, BL_PACK_BASE3, BL_PACK_1BIT or other N
- * return BL_ERR_UNSUPPORTED. Dimensions above 2^24 return BL_ERR_INVALID_ARG.
+ * Requires N % 8 == 0. BL_F32 grad_y or other N return BL_ERR_UNSUPPORTED.
+ * Dimensions above 2^24 return BL_ERR_INVALID_ARG.
  * M = 0 is a no-op; N = 0 writes zeros. */
 bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,
                                    int layout, const float *gamma, int64_t M, int64_t N,

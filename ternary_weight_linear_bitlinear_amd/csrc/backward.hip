@@ -54,7 +54,7 @@ struct BwdCfg {
     static_assert(BI == BJ, "one padded [p][*] row length serves A and B");
 };
 
-enum { kBDense = 0, kBPacked2 = 1 };
+enum { kBDense = 0, kBPacked2 = 1, kBPacked1 = 2, kBPacked3 = 3 };
 
 // Four codes of one 2-bit field (bytes u = c + 1 in 0..2) to four bf16 values
 // -1 / 0 / +1 (0xBF80 / 0x0000 / 0x3F80) in two dwords. The byte permute picks
@@ -67,6 +67,34 @@ __device__ __forceinline__ void field_to_bf16(uint32_t f, uint32_t &d0, uint32_t
     const uint32_t s1 = __builtin_amdgcn_perm(f4, f, 0x07030602u);  // u2, u2+4, u3, u3+4
     d0 = __builtin_amdgcn_perm(kHi, kLo, s0);
     d1 = __builtin_amdgcn_perm(kHi, kLo, s1);
+}
+
+// Eight bytes of the base-3 layout (five codes each, first code in the least
+// significant trit) as 40 fields u = c + 1 in 0..2, one per byte, in five
+// 64-bit words; then the 32 fields starting at field `first` (0..4) as eight
+// words of four fields each (natural order).
+__device__ __forceinline__ void base3_fields(const uint32_t (&b)[8], int first, uint32_t (&out)[8]) {
+    uint64_t f[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t v = b[i];
+#pragma unroll
+        for (int r = 0; r < 5; ++r) {
+            const uint32_t q = v / 3u;
+            const int g = 5 * i + r;  // field index: byte g of the 40-byte string
+            f[g / 8] |= (uint64_t)(v - 3u * q) << (8 * (g % 8));
+            v = q;
+        }
+    }
+    const int sh = 8 * first;  // 0 .. 32
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint64_t lo = f[w] >> sh;
+        const uint64_t hi = sh == 0 ? 0 : f[w + 1] << (64 - sh);
+        const uint64_t v = lo | hi;
+        out[2 * w] = (uint32_t)v;
+        out[2 * w + 1] = (uint32_t)(v >> 32);
+    }
 }
 
 template <bool A_T, int BSRC>
@@ -126,13 +154,36 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                 b_ok[c] = p < P && j < J;
                 b_reg[c] = *reinterpret_cast<const v4i *>(B16 + (b_ok[c] ? p * ldb + j : 0));
             }
-        } else {
+        } else if constexpr (BSRC == kBPacked2) {
             // 64 rows x 64 packed bytes: 8 bytes (32 codes) per thread
             const int64_t p = p0 + tid / 8;
             const int64_t byte = j0 / 4 + 8 * (tid % 8);
             b_ok[0] = p < P && byte + 8 <= ldb;
             const uint2 v = *reinterpret_cast<const uint2 *>(B8 + (b_ok[0] ? p * ldb + byte : 0));
             b_reg[0] = v4i{(int)v.x, (int)v.y, 0, 0};
+        } else if constexpr (BSRC == kBPacked1) {
+            // 64 rows x 32 packed bytes: one 32-code word per thread
+            const int64_t p = p0 + tid / 8;
+            const int64_t byte = j0 / 8 + 4 * (tid % 8);
+            b_ok[0] = p < P && byte + 4 <= ldb;
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(B8 + (b_ok[0] ? p * ldb + byte : 0));
+            b_reg[0] = v4i{(int)v, 0, 0, 0};
+        } else {
+            // base-3: the eight bytes holding codes c0 .. c0 + 31 start at byte
+            // c0 / 5; bytes past the row read as 121 (five zero codes)
+            const int64_t p = p0 + tid / 8;
+            const int64_t c0 = j0 + 32 * (tid % 8);
+            const int64_t b0 = c0 / 5;
+            const bool row_ok = p < P;
+            const uint8_t *row = B8 + (row_ok ? p : 0) * ldb;
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t v = row_ok && b0 + i < ldb ? row[b0 + i] : 121u;
+                w[i / 4] |= v << (8 * (i % 4));
+            }
+            b_ok[0] = row_ok;
+            b_reg[0] = v4i{(int)w[0], (int)w[1], (int)(c0 - 5 * b0), 0};
         }
     };
 
@@ -154,6 +205,35 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                 const int off = (q / (G::BJ / 8)) * G::LD_PX + 16 * (q % (G::BJ / 8));
                 *reinterpret_cast<v4i *>(Bs + off) = b_ok[c] ? b_reg[c] : z;
             }
+        } else if constexpr (BSRC == kBPacked1) {
+            // bit t of byte i of the word is code 4 t + i; u = 2 bit (0 or 2)
+            // picks -1 or +1. Rows past P multiply zeros of A.
+            const uint32_t word = (uint32_t)b_reg[0][0];
+            uint8_t *dst = Bs + (tid / 8) * G::LD_PX + 64 * (tid % 8);
+            uint32_t d[16];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                field_to_bf16(((word >> t) & 0x01010101u) << 1, d[2 * t], d[2 * t + 1]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint4 *>(dst + 16 * q) =
+                    make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+        } else if constexpr (BSRC == kBPacked3) {
+            const uint32_t bytes[8] = {
+                (uint32_t)b_reg[0][0] & 0xFFu, ((uint32_t)b_reg[0][0] >> 8) & 0xFFu,
+                ((uint32_t)b_reg[0][0] >> 16) & 0xFFu, (uint32_t)b_reg[0][0] >> 24,
+                (uint32_t)b_reg[0][1] & 0xFFu, ((uint32_t)b_reg[0][1] >> 8) & 0xFFu,
+                ((uint32_t)b_reg[0][1] >> 16) & 0xFFu, (uint32_t)b_reg[0][1] >> 24};
+            uint32_t f[8];
+            base3_fields(bytes, b_reg[0][2], f);
+            uint8_t *dst = Bs + (tid / 8) * G::LD_PX + 64 * (tid % 8);
+            uint32_t d[16];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) field_to_bf16(f[w], d[2 * w], d[2 * w + 1]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint4 *>(dst + 16 * q) =
+                    make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
         } else {
             // word w holds codes 16 w .. 16 w + 15 of the piece; field s of a
             // word holds its codes 4 s .. 4 s + 3 (one per byte)
@@ -281,9 +361,15 @@ hipError_t launch_zero_f32(float *out, int64_t count, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_backward_input(const uint16_t *grad_y, const uint8_t *packed, const float *gamma,
-                                 int64_t M, int64_t N, int64_t K, float *grad_x,
-                                 hipStream_t stream) {
+hipError_t launch_backward_input(const uint16_t *grad_y, const uint8_t *packed, int layout,
+                                 const float *gamma, int64_t M, int64_t N, int64_t K,
+                                 float *grad_x, hipStream_t stream) {
+    if (layout == kLayout1Bit)
+        return launch_bwd<false, kBPacked1>(grad_y, N, packed, row_bytes_1bit(K), M, K, N, gamma,
+                                            grad_x, K, stream);
+    if (layout == kLayoutBase3)
+        return launch_bwd<false, kBPacked3>(grad_y, N, packed, row_bytes_base3(K), M, K, N, gamma,
+                                            grad_x, K, stream);
     return launch_bwd<false, kBPacked2>(grad_y, N, packed, row_bytes_2bit(K), M, K, N, gamma,
                                         grad_x, K, stream);
 }

@@ -47,13 +47,23 @@ def check_sum(got: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, n: int, wha
     return worst
 
 
-def packed_problem(bl, M, N, K, seed, scheme="ternary"):
+def packed_problem(bl, M, N, K, seed, scheme="ternary", layout="2bit"):
     p = synth.make_problem(M=M, N=N, K=K, seed=seed, dtype="bf16", grad_std=1e-3)
-    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, True), "2bit", scheme)
+    packed, gamma = bl.bitlinear_pack_weights(dev(p.w_store, True), layout, scheme)
     torch.cuda.synchronize()
-    codes, bad = oracle.unpack(to_np(packed), K, "2bit")  # the codes the GPU will use
+    codes, bad = oracle.unpack(to_np(packed), K, layout)  # the codes the GPU will use
     assert bad == 0
     return p, packed, gamma, codes, float(to_np(gamma)[0])
+
+
+def check_grad_x(bl, p, packed, gamma, codes, g, layout, rows=None):
+    gx = to_np(bl.bitlinear_backward_input(dev(p.grad_y_store, True), packed, gamma, p.K, layout))
+    gy = p.grad_y if rows is None else np.ascontiguousarray(p.grad_y[rows])
+    if rows is not None:
+        gx = gx[rows]
+    ref = oracle.ste_grad_x(gy, codes, g)
+    abs_sum = (np.abs(gy.astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
+    return check_sum(gx, ref, abs_sum, p.N, f"grad_x ({layout})")
 
 
 BWD_CASES = [
@@ -62,15 +72,18 @@ BWD_CASES = [
 ]
 
 
+SCHEME = {"2bit": "ternary", "base3": "ternary", "1bit": "binary"}
+
+
+@pytest.mark.parametrize("layout", ["2bit", "base3", "1bit"])
 @pytest.mark.parametrize("M,N,K", BWD_CASES)
-def test_backward_input_parity(bl, M, N, K):
-    banner(f"backward_input M={M} N={N} K={K}")
-    p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=500 + M + N + K)
-    gx = bl.bitlinear_backward_input(dev(p.grad_y_store, True), packed, gamma, K)
-    torch.cuda.synchronize()
-    ref = oracle.ste_grad_x(p.grad_y, codes, g)
-    abs_sum = (np.abs(p.grad_y.astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
-    check_sum(to_np(gx), ref, abs_sum, N, "grad_x")
+def test_backward_input_parity(bl, M, N, K, layout):
+    """grad_x straight from the forward's packed rows in each layout (ternary
+    codes for 2-bit and base-3, binary codes for the 1-bit layout)."""
+    banner(f"backward_input {layout} M={M} N={N} K={K}")
+    p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=500 + M + N + K,
+                                                scheme=SCHEME[layout], layout=layout)
+    check_grad_x(bl, p, packed, gamma, codes, g, layout)
 
 
 @pytest.mark.parametrize("M,N,K", [c for c in BWD_CASES if c[2] % 8 == 0])
@@ -84,29 +97,56 @@ def test_backward_weight_parity(bl, M, N, K):
     check_sum(to_np(gw), ref, abs_sum, M, "grad_w")
 
 
-def test_backward_input_ragged_k(bl):
-    """K not a multiple of 8 (the packed rows end inside a 16-code group)."""
-    M, N, K = 40, 96, 1001
-    banner(f"backward_input ragged K M={M} N={N} K={K}")
-    p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=77)
-    gx = bl.bitlinear_backward_input(dev(p.grad_y_store, True), packed, gamma, K)
-    torch.cuda.synchronize()
-    ref = oracle.ste_grad_x(p.grad_y, codes, g)
-    abs_sum = (np.abs(p.grad_y.astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
-    check_sum(to_np(gx), ref, abs_sum, N, "grad_x")
+@pytest.mark.parametrize("layout", ["2bit", "base3", "1bit"])
+@pytest.mark.parametrize("K", [1001, 5, 255, 261, 1281])
+def test_backward_input_ragged_k(bl, layout, K):
+    """K not a multiple of the tile width nor of a layout's code group (16-code
+    words of the 2-bit layout, 5-code bytes of base-3, 32-code words of 1-bit):
+    the rows end inside a group, and for base-3 a thread's 32 codes start
+    inside a byte (K = 261, 1281 put a tile edge mid-byte)."""
+    M, N = 40, 96
+    banner(f"backward_input ragged K {layout} M={M} N={N} K={K}")
+    p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=77 + K,
+                                                scheme=SCHEME[layout], layout=layout)
+    check_grad_x(bl, p, packed, gamma, codes, g, layout)
 
 
 def test_backward_input_binary_codes(bl):
-    """1-bit codes (+-1 in the 2-bit container) through the same product."""
+    """1-bit codes (+-1 in the 2-bit container) through the 2-bit product."""
     M, N, K = 128, 256, 320
     banner(f"backward_input binary M={M} N={N} K={K}")
     p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=88, scheme="binary")
     assert set(np.unique(codes)) <= {-1, 1}
-    gx = bl.bitlinear_backward_input(dev(p.grad_y_store, True), packed, gamma, K)
-    torch.cuda.synchronize()
+    check_grad_x(bl, p, packed, gamma, codes, g, "2bit")
+
+
+@pytest.mark.parametrize("layout", ["base3", "1bit"])
+def test_backward_input_every_code_pattern(bl, layout):
+    """Every byte value of the layout in every position of a row: base-3 bytes
+    0..242 and 1-bit bytes 0..255, so every trit or bit place of every byte
+    (and every offset of a 32-code run inside base-3 bytes) meets the
+    expansion to bf16. The codes are the oracle's unpacking of the bytes."""
+    K = {"base3": 243 * 5, "1bit": 256 * 8}[layout]
+    rb = bl.bitlinear_packed_row_bytes(K, layout)
+    N, M = 64, 48
+    banner(f"backward_input every code pattern {layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(4)
+    nvals = 243 if layout == "base3" else 256
+    packed_np = np.zeros((N, rb), np.uint8)
+    for n in range(N):
+        packed_np[n, :nvals] = np.roll(np.arange(nvals, dtype=np.uint8), 7 * n)
+    if layout == "base3":
+        packed_np[:, nvals:] = 121  # five zero codes
+    codes, bad = oracle.unpack(packed_np, K, layout)
+    assert bad == 0
+    p = synth.make_problem(M=M, N=N, K=K, seed=41, dtype="bf16", grad_std=1e-3)
+    g = 0.75
+    gamma = torch.tensor([g], dtype=torch.float32, device="cuda")
+    gx = to_np(bl.bitlinear_backward_input(dev(p.grad_y_store, True), dev(packed_np), gamma, K,
+                                           layout))
     ref = oracle.ste_grad_x(p.grad_y, codes, g)
     abs_sum = (np.abs(p.grad_y.astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
-    check_sum(to_np(gx), ref, abs_sum, N, "grad_x")
+    check_sum(gx, ref, abs_sum, N, f"grad_x ({layout})")
 
 
 def test_backward_empty_sums_write_zeros(bl):
@@ -136,13 +176,10 @@ def test_training_shapes_sampled(bl):
     banner(f"backward training shapes M={M} N={N} K={K}")
     p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=cfg["seed"])
     gy = dev(p.grad_y_store, True)
-    gx = to_np(bl.bitlinear_backward_input(gy, packed, gamma, K))
     gw = to_np(bl.bitlinear_backward_weight(gy, dev(p.x_store, True)))
     rng = np.random.default_rng(5)
     rows = np.sort(rng.choice(M, 6, replace=False))
-    ref = oracle.ste_grad_x(p.grad_y[rows], codes, g)
-    abs_sum = (np.abs(p.grad_y[rows].astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
-    check_sum(gx[rows], ref, abs_sum, N, "grad_x rows")
+    check_grad_x(bl, p, packed, gamma, codes, g, "2bit", rows=rows)
     cols = np.sort(rng.choice(N, 6, replace=False))
     ref = oracle.ste_grad_w(np.ascontiguousarray(p.grad_y[:, cols]), p.x)
     abs_sum = np.abs(p.grad_y[:, cols].astype(np.float64)).T @ np.abs(p.x.astype(np.float64))
