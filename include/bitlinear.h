@@ -231,12 +231,17 @@ bl_status bitlinear_forward_lut(const int8_t *xq, const float *scale, const uint
  * Both run on the bf16 matrix cores with fp32 accumulation.
  *
  * bitlinear_backward_input: grad_x[m,k] = gamma * sum_n grad_y[m,n] * c[n,k].
- *   grad_y  [M, N] bf16 (gy_dtype must be BL_BF16).
+ *   grad_y  [M, N], gy_dtype BL_BF16 or BL_F32. fp32 values are split exactly
+ *           into three bf16 pieces (hi + mid + lo, 8 significant bits each) and
+ *           the contraction runs over all three into one fp32 sum, so each
+ *           product term is still exact (for |grad_y| >= 2^-110; smaller
+ *           values may lose bits below 2^-133). Three times the matrix-core
+ *           work of bf16 grad_y.
  *   packed  [N, row_bytes] codes in `layout` (BL_PACK_2BIT, BL_PACK_BASE3 or
  *           BL_PACK_1BIT: the forward's own matrix; no transposed copy is
  *           needed); gamma: 1 float (device).
  *   grad_x  out: [M, K] fp32.
- * Requires N % 8 == 0. BL_F32 grad_y or other N return BL_ERR_UNSUPPORTED.
+ * Requires N % 8 == 0 (else BL_ERR_UNSUPPORTED).
  * Dimensions above 2^24 return BL_ERR_INVALID_ARG.
  * M = 0 is a no-op; N = 0 writes zeros. */
 bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8_t *packed,

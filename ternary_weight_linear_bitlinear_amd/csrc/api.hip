@@ -254,14 +254,14 @@ bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8
     if (M < 0 || N < 0 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return BL_ERR_INVALID_ARG;
     if (!valid_dtype(gy_dtype) || !valid_layout(layout)) return BL_ERR_INVALID_ARG;
-    if (gy_dtype != BL_BF16 || N % 8 != 0) return BL_ERR_UNSUPPORTED;
+    if (N % 8 != 0) return BL_ERR_UNSUPPORTED;
     if (M == 0) return BL_OK;
     bl_status st = device_ok();
     if (st != BL_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (N == 0) return launched(bl::launch_zero_f32(grad_x, M * K, s));
-    return launched(bl::launch_backward_input(static_cast<const uint16_t *>(grad_y), packed,
-                                              layout, gamma, M, N, K, grad_x, s));
+    return launched(bl::launch_backward_input(grad_y, gy_dtype == BL_F32, packed, layout, gamma,
+                                              M, N, K, grad_x, s));
 }
 
 bl_status bitlinear_backward_weight(const void *grad_y, const void *x, int dtype, int64_t M,

@@ -51,6 +51,7 @@ struct BwdCfg {
     static constexpr int B_BYTES = BP * LD_PX;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int SMEM = 2 * STAGE;
+    static constexpr int LUT3 = 256 * 8;  // base-3 byte -> five fields (after the stages)
     static_assert(BI == BJ, "one padded [p][*] row length serves A and B");
 };
 
@@ -69,22 +70,35 @@ __device__ __forceinline__ void field_to_bf16(uint32_t f, uint32_t &d0, uint32_t
     d1 = __builtin_amdgcn_perm(kHi, kLo, s1);
 }
 
-// Eight bytes of the base-3 layout (five codes each, first code in the least
-// significant trit) as 40 fields u = c + 1 in 0..2, one per byte, in five
-// 64-bit words; then the 32 fields starting at field `first` (0..4) as eight
-// words of four fields each (natural order).
-__device__ __forceinline__ void base3_fields(const uint32_t (&b)[8], int first, uint32_t (&out)[8]) {
+// Base-3 decode table entry for byte v: its five trits t_r = c_r + 1 (first
+// code in the least significant trit) as one field per byte, bytes 0..4.
+// Bytes 243..255 are not produced by the packing; they read as five zero codes.
+__device__ __forceinline__ uint64_t base3_field_entry(uint32_t v) {
+    if (v >= 243u) return 0x0101010101ull;
+    uint64_t e = 0;
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+        e |= (uint64_t)(v % 3u) << (8 * r);
+        v /= 3u;
+    }
+    return e;
+}
+
+// Eight bytes of the base-3 layout (words w0, w1, first byte in the low bits)
+// as their 40 fields, one per byte, looked up in the table; then the 32 fields
+// starting at field `first` (0..4) as eight words of four fields each
+// (natural order).
+__device__ __forceinline__ void base3_fields(uint32_t w0, uint32_t w1, int first,
+                                             const uint64_t *lut, uint32_t (&out)[8]) {
     uint64_t f[5] = {0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        uint32_t v = b[i];
-#pragma unroll
-        for (int r = 0; r < 5; ++r) {
-            const uint32_t q = v / 3u;
-            const int g = 5 * i + r;  // field index: byte g of the 40-byte string
-            f[g / 8] |= (uint64_t)(v - 3u * q) << (8 * (g % 8));
-            v = q;
-        }
+        const uint32_t v = ((i < 4 ? w0 : w1) >> (8 * (i % 4))) & 0xFFu;
+        const uint64_t e = lut[v];
+        constexpr int kSh[8] = {0, 40, 16, 56, 32, 8, 48, 24};  // 8 * (5 i % 8)
+        const int w = (5 * i) / 8, sh = kSh[i];
+        f[w] |= e << sh;
+        if (sh > 24) f[w + 1] |= e >> (64 - sh);
     }
     const int sh = 8 * first;  // 0 .. 32
 #pragma unroll
@@ -97,13 +111,37 @@ __device__ __forceinline__ void base3_fields(const uint32_t (&b)[8], int first, 
     }
 }
 
-template <bool A_T, int BSRC>
+// The top halves of two fp32 words as one word of two bf16 values.
+__device__ __forceinline__ uint32_t top_halves(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Piece `piece` of the exact three-way bf16 split of fp32 values x = hi + mid
+// + lo: hi is x with its low 16 bits cleared, mid the same of x - hi, lo =
+// x - hi - mid. Each subtraction is exact, and the pieces carry 8 + 8 + 8 of
+// x's 24 significant bits, so every piece is a bf16 value (for |x| >= 2^-110;
+// below that lo can fall among fp32 subnormals and lose bits under 2^-133).
+// All pieces share x's sign, so |hi| + |mid| + |lo| = |x|.
+__device__ __forceinline__ uint32_t f32_piece_bits(uint32_t ux, int piece) {
+    if (piece == 0) return ux;
+    const float x = __uint_as_float(ux);
+    const float r = x - __uint_as_float(ux & 0xFFFF0000u);
+    const uint32_t ur = __float_as_uint(r);
+    if (piece == 1) return ur;
+    return __float_as_uint(r - __uint_as_float(ur & 0xFFFF0000u));
+}
+
+// A_F32 (grad_x only): A holds fp32 values; the contraction runs three times
+// over p, once per bf16 piece of A (hi, mid, lo), into the same accumulators.
+template <bool A_T, int BSRC, bool A_F32 = false>
 __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
-    const uint16_t *__restrict__ A, int64_t lda, const void *__restrict__ Bv, int64_t ldb,
+    const void *__restrict__ Av, int64_t lda, const void *__restrict__ Bv, int64_t ldb,
     int64_t I, int64_t J, int64_t P, const float *__restrict__ alpha_p, int tiles_i,
     int tiles_j, float *__restrict__ C, int64_t ldc) {
     using G = BwdCfg;
+    static_assert(!A_F32 || !A_T, "fp32 A only as stored [i][p]");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint64_t *lut = reinterpret_cast<uint64_t *>(smem + G::SMEM);  // base-3 only
 
     const int ntiles = tiles_i * tiles_j;
     const int per_xcd = (ntiles + kXcds - 1) / kXcds;
@@ -120,10 +158,13 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
     // ---- global -> register staging, one contraction slice per stage ------
     constexpr int A_CH = G::BI * G::BP / 8 / G::kThreads;  // 16-byte chunks per thread
     constexpr int B_CH = BSRC == kBDense ? G::BP * G::BJ / 8 / G::kThreads : 1;
-    v4i a_reg[A_CH];
+    constexpr int A_W = A_F32 ? 2 : 1;  // 16-byte loads per chunk of 8 values
+    v4i a_reg[A_CH][A_W];
     bool a_ok[A_CH];
     v4i b_reg[B_CH];  // dense: 16-byte chunks; packed: one 8-byte piece in lanes 0, 1
     bool b_ok[B_CH];
+    const uint16_t *A16 = static_cast<const uint16_t *>(Av);
+    const float *A32 = static_cast<const float *>(Av);
     const uint16_t *B16 = static_cast<const uint16_t *>(Bv);
     const uint8_t *B8 = static_cast<const uint8_t *>(Bv);
 
@@ -144,7 +185,13 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                 a_ok[c] = p < P && i < I;
                 off = p * lda + i;
             }
-            a_reg[c] = *reinterpret_cast<const v4i *>(A + (a_ok[c] ? off : 0));
+            if constexpr (A_F32) {
+                const v4i *src = reinterpret_cast<const v4i *>(A32 + (a_ok[c] ? off : 0));
+                a_reg[c][0] = src[0];
+                a_reg[c][1] = src[1];
+            } else {
+                a_reg[c][0] = *reinterpret_cast<const v4i *>(A16 + (a_ok[c] ? off : 0));
+            }
         }
         if constexpr (BSRC == kBDense) {
 #pragma unroll
@@ -170,24 +217,26 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
             b_reg[0] = v4i{(int)v, 0, 0, 0};
         } else {
             // base-3: the eight bytes holding codes c0 .. c0 + 31 start at byte
-            // c0 / 5; bytes past the row read as 121 (five zero codes)
+            // b0 = c0 / 5, inside the three aligned dwords from b0 & ~3 (row
+            // bytes are a multiple of 16, so each dword is wholly inside or
+            // past the row; those past it read as 121 = five zero codes)
             const int64_t p = p0 + tid / 8;
             const int64_t c0 = j0 + 32 * (tid % 8);
-            const int64_t b0 = c0 / 5;
+            const int64_t b0 = c0 / 5, al = b0 & ~(int64_t)3;
             const bool row_ok = p < P;
-            const uint8_t *row = B8 + (row_ok ? p : 0) * ldb;
-            uint32_t w[2] = {0u, 0u};
+            const uint32_t *row = reinterpret_cast<const uint32_t *>(B8 + (row_ok ? p : 0) * ldb);
+            uint32_t d[3];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t v = row_ok && b0 + i < ldb ? row[b0 + i] : 121u;
-                w[i / 4] |= v << (8 * (i % 4));
-            }
+            for (int i = 0; i < 3; ++i)
+                d[i] = row_ok && al + 4 * i < ldb ? row[al / 4 + i] : 0x79797979u;
+            const uint32_t sh = (uint32_t)(b0 - al);
             b_ok[0] = row_ok;
-            b_reg[0] = v4i{(int)w[0], (int)w[1], (int)(c0 - 5 * b0), 0};
+            b_reg[0] = v4i{(int)__builtin_amdgcn_alignbyte(d[1], d[0], sh),
+                           (int)__builtin_amdgcn_alignbyte(d[2], d[1], sh), (int)(c0 - 5 * b0), 0};
         }
     };
 
-    auto store_stage = [&](uint8_t *st) __attribute__((always_inline)) {
+    auto store_stage = [&](uint8_t *st, int piece) __attribute__((always_inline)) {
         uint8_t *As = st;
         uint8_t *Bs = st + G::A_BYTES;
         const v4i z = {0, 0, 0, 0};
@@ -196,7 +245,17 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
             const int q = tid + c * G::kThreads;
             const int off = !A_T ? (q / (G::BP / 8)) * G::LD_IP + 16 * (q % (G::BP / 8))
                                  : (q / (G::BI / 8)) * G::LD_PX + 16 * (q % (G::BI / 8));
-            *reinterpret_cast<v4i *>(As + off) = a_ok[c] ? a_reg[c] : z;
+            v4i v;
+            if constexpr (A_F32) {
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = f32_piece_bits((uint32_t)a_reg[c][e / 4][e % 4], piece);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (int)top_halves(h[2 * e], h[2 * e + 1]);
+            } else {
+                v = a_reg[c][0];
+            }
+            *reinterpret_cast<v4i *>(As + off) = a_ok[c] ? v : z;
         }
         if constexpr (BSRC == kBDense) {
 #pragma unroll
@@ -219,13 +278,8 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                 *reinterpret_cast<uint4 *>(dst + 16 * q) =
                     make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
         } else if constexpr (BSRC == kBPacked3) {
-            const uint32_t bytes[8] = {
-                (uint32_t)b_reg[0][0] & 0xFFu, ((uint32_t)b_reg[0][0] >> 8) & 0xFFu,
-                ((uint32_t)b_reg[0][0] >> 16) & 0xFFu, (uint32_t)b_reg[0][0] >> 24,
-                (uint32_t)b_reg[0][1] & 0xFFu, ((uint32_t)b_reg[0][1] >> 8) & 0xFFu,
-                ((uint32_t)b_reg[0][1] >> 16) & 0xFFu, (uint32_t)b_reg[0][1] >> 24};
             uint32_t f[8];
-            base3_fields(bytes, b_reg[0][2], f);
+            base3_fields((uint32_t)b_reg[0][0], (uint32_t)b_reg[0][1], b_reg[0][2], lut, f);
             uint8_t *dst = Bs + (tid / 8) * G::LD_PX + 64 * (tid % 8);
             uint32_t d[16];
 #pragma unroll
@@ -301,15 +355,23 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
         }
     };
 
-    const int64_t nst = (P + G::BP - 1) / G::BP;
+    if constexpr (BSRC == kBPacked3) {
+        if (tid < 256) lut[tid] = base3_field_entry((uint32_t)tid);
+        __syncthreads();
+    }
+    // stage s: contraction slice s % per_piece, piece s / per_piece of fp32 A
+    const int64_t per_piece = (P + G::BP - 1) / G::BP;
+    const int64_t nst = per_piece * (A_F32 ? 3 : 1);
+    auto slice_of = [&](int64_t s) { return (A_F32 ? s % per_piece : s) * G::BP; };
+    auto piece_of = [&](int64_t s) { return A_F32 ? (int)(s / per_piece) : 0; };
     load_stage(0);
-    store_stage(smem);
+    store_stage(smem, 0);
     __syncthreads();
     for (int64_t s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
-        if (more) load_stage((s + 1) * G::BP);
+        if (more) load_stage(slice_of(s + 1));
         compute(smem + (s & 1) * G::STAGE);
-        if (more) store_stage(smem + ((s + 1) & 1) * G::STAGE);
+        if (more) store_stage(smem + ((s + 1) & 1) * G::STAGE, piece_of(s + 1));
         lds_barrier();
     }
 
@@ -330,18 +392,19 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
         }
 }
 
-template <bool A_T, int BSRC>
-hipError_t launch_bwd(const uint16_t *A, int64_t lda, const void *B, int64_t ldb, int64_t I,
+template <bool A_T, int BSRC, bool A_F32 = false>
+hipError_t launch_bwd(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t I,
                       int64_t J, int64_t P, const float *alpha, float *C, int64_t ldc,
                       hipStream_t s) {
     using G = BwdCfg;
     const int ti = (int)((I + G::BI - 1) / G::BI), tj = (int)((J + G::BJ - 1) / G::BJ);
     const int64_t blocks = ((int64_t)ti * tj + kXcds - 1) / kXcds * kXcds;
-    auto kern = bwd_gemm_kernel<A_T, BSRC>;
+    auto kern = bwd_gemm_kernel<A_T, BSRC, A_F32>;
+    const int smem = G::SMEM + (BSRC == kBPacked3 ? G::LUT3 : 0);
     static LdsFlag lds_raised{0};
-    hipError_t e = allow_dynamic_lds(kern, G::SMEM, &lds_raised);
+    hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(G::kThreads), G::SMEM, s, A, lda, B,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(G::kThreads), smem, s, A, lda, B,
                        ldb, I, J, P, alpha, ti, tj, C, ldc);
     return hipGetLastError();
 }
@@ -361,17 +424,28 @@ hipError_t launch_zero_f32(float *out, int64_t count, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_backward_input(const uint16_t *grad_y, const uint8_t *packed, int layout,
-                                 const float *gamma, int64_t M, int64_t N, int64_t K,
-                                 float *grad_x, hipStream_t stream) {
+namespace {
+template <bool F32>
+hipError_t backward_input_t(const void *grad_y, const uint8_t *packed, int layout,
+                            const float *gamma, int64_t M, int64_t N, int64_t K, float *grad_x,
+                            hipStream_t stream) {
     if (layout == kLayout1Bit)
-        return launch_bwd<false, kBPacked1>(grad_y, N, packed, row_bytes_1bit(K), M, K, N, gamma,
-                                            grad_x, K, stream);
+        return launch_bwd<false, kBPacked1, F32>(grad_y, N, packed, row_bytes_1bit(K), M, K, N,
+                                                 gamma, grad_x, K, stream);
     if (layout == kLayoutBase3)
-        return launch_bwd<false, kBPacked3>(grad_y, N, packed, row_bytes_base3(K), M, K, N, gamma,
-                                            grad_x, K, stream);
-    return launch_bwd<false, kBPacked2>(grad_y, N, packed, row_bytes_2bit(K), M, K, N, gamma,
-                                        grad_x, K, stream);
+        return launch_bwd<false, kBPacked3, F32>(grad_y, N, packed, row_bytes_base3(K), M, K, N,
+                                                 gamma, grad_x, K, stream);
+    return launch_bwd<false, kBPacked2, F32>(grad_y, N, packed, row_bytes_2bit(K), M, K, N, gamma,
+                                             grad_x, K, stream);
+}
+}  // namespace
+
+hipError_t launch_backward_input(const void *grad_y, bool grad_y_f32, const uint8_t *packed,
+                                 int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                                 float *grad_x, hipStream_t stream) {
+    return grad_y_f32 ? backward_input_t<true>(grad_y, packed, layout, gamma, M, N, K, grad_x, stream)
+                      : backward_input_t<false>(grad_y, packed, layout, gamma, M, N, K, grad_x,
+                                                stream);
 }
 
 hipError_t launch_backward_weight(const uint16_t *grad_y, const uint16_t *x, int64_t M, int64_t N,

@@ -174,10 +174,10 @@ hipError_t launch_forward_lut(const int8_t *xq, const float *scale, const uint8_
                               int32_t *acc, hipStream_t stream);
 
 // ---- backward products (backward.hip) ------------------------------------
-// grad_x [M, K] fp32 = gamma * grad_y [M, N] (bf16) x codes of packed [N, row_bytes] in
-// `layout` (2-bit, base-3 or 1-bit).
-hipError_t launch_backward_input(const uint16_t *grad_y, const uint8_t *packed, int layout,
-                                 const float *gamma, int64_t M, int64_t N, int64_t K,
+// grad_x [M, K] fp32 = gamma * grad_y [M, N] (bf16, or fp32 when grad_y_f32) x codes of
+// packed [N, row_bytes] in `layout` (2-bit, base-3 or 1-bit).
+hipError_t launch_backward_input(const void *grad_y, bool grad_y_f32, const uint8_t *packed,
+                                 int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                                  float *grad_x, hipStream_t stream);
 // grad_w [N, K] fp32 = grad_y^T (bf16 [M, N]) x x (bf16 [M, K]).
 hipError_t launch_backward_weight(const uint16_t *grad_y, const uint16_t *x, int64_t M,

@@ -155,9 +155,8 @@ def test_backward_rejects_and_limits(bl):
     assert bi(N=(1 << 24) + 8) == bl.BL_ERR_INVALID_ARG
     assert bi(dt=5) == bl.BL_ERR_INVALID_ARG
     assert bi(layout=4) == bl.BL_ERR_INVALID_ARG
-    assert bi(dt=0) == bl.BL_ERR_UNSUPPORTED       # fp32 grad_y
     assert bi(N=60) == bl.BL_ERR_UNSUPPORTED       # N % 8 != 0
-    assert bi(layout=1, dt=0) == bl.BL_ERR_UNSUPPORTED
+    assert bi(layout=1, dt=0, N=4) == bl.BL_ERR_UNSUPPORTED
     assert bi(layout=2, N=60) == bl.BL_ERR_UNSUPPORTED
     assert bi(M=0) == bl.BL_OK
     bw = lambda **kw: lib.bitlinear_backward_weight(kw.get("gy", P), kw.get("x", P),

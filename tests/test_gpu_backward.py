@@ -111,6 +111,45 @@ def test_backward_input_ragged_k(bl, layout, K):
     check_grad_x(bl, p, packed, gamma, codes, g, layout)
 
 
+@pytest.mark.parametrize("layout", ["2bit", "base3", "1bit"])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 520, 264), (33, 8, 1000), (17, 264, 2056)])
+def test_backward_input_fp32_grad(bl, M, N, K, layout):
+    """fp32 grad_y: each value is split exactly into three bf16 pieces and the
+    3N products of the pieces with the codes are summed in fp32, so the bound
+    is the fp32 summation bound over 3N terms (|hi| + |mid| + |lo| = |g|, so
+    the sum of |terms| is unchanged). At N = 8 the bound is ~1.4e-6 of the sum
+    of |terms|: losing the low piece (2^-16 relative) would fail it."""
+    banner(f"backward_input fp32 grad_y {layout} M={M} N={N} K={K}")
+    p, packed, gamma, codes, g = packed_problem(bl, M, N, K, seed=900 + M + N + K,
+                                                scheme=SCHEME[layout], layout=layout)
+    gy = np.ascontiguousarray(p.grad_y, np.float32)
+    gx = to_np(bl.bitlinear_backward_input(dev(gy), packed, gamma, K, layout))
+    ref = oracle.ste_grad_x(gy, codes, g)
+    abs_sum = (np.abs(gy.astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
+    check_sum(gx, ref, abs_sum, 3 * N, f"grad_x fp32 ({layout})")
+
+
+def test_backward_input_fp32_wide_range(bl):
+    """fp32 grad_y with full 24-bit significands over exponents 2^-100 .. 2^30
+    and both signs, against codes of all +1 in a few columns (so each output is
+    a plain sum whose low bits come from the mid and lo pieces)."""
+    M, N, K = 96, 16, 64
+    banner(f"backward_input fp32 wide range M={M} N={N} K={K}")
+    rng = np.random.default_rng(12)
+    mant = 1.0 + rng.integers(0, 1 << 23, size=(M, N)) / float(1 << 23)
+    expo = rng.integers(-100, 31, size=(M, N))
+    gy = (np.where(rng.random((M, N)) < 0.5, -1.0, 1.0) * mant * np.exp2(expo)).astype(np.float32)
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    codes[:, :4] = 1
+    packed_np = oracle.pack(codes, "2bit")
+    g = 1.0
+    gamma = torch.tensor([g], dtype=torch.float32, device="cuda")
+    gx = to_np(bl.bitlinear_backward_input(dev(gy), dev(packed_np), gamma, K, "2bit"))
+    ref = oracle.ste_grad_x(gy, codes, g)
+    abs_sum = np.abs(gy.astype(np.float64)) @ np.abs(codes.astype(np.float64))
+    check_sum(gx, ref, abs_sum, 3 * N, "grad_x fp32 wide range")
+
+
 def test_backward_input_binary_codes(bl):
     """1-bit codes (+-1 in the 2-bit container) through the 2-bit product."""
     M, N, K = 128, 256, 320
