@@ -275,6 +275,18 @@ def main():
                                     blocks=best[1], loads_in_flight=best[2],
                                     what="one 4 MiB buffer per launch, 128 rotating, cold caches")
     del bufs
+    # the same over one 32 MiB buffer per launch (the 32768 x 4096 weight
+    # stream below), 16 rotating buffers
+    bufs = [torch.randint(0, 256, (32 << 20,), dtype=torch.uint8, device=dev) for _ in range(16)]
+    best = None
+    for blocks, unroll in ((1024, 2), (2048, 1), (512, 4), (1024, 4), (2048, 2)):
+        ms = graph_ms(lambda i, b=blocks, u=unroll: probe_read(bufs[i % 16], b, u), 64)
+        if best is None or ms < best[0]:
+            best = (ms, blocks, unroll)
+    ceil["stream_read_32MiB"] = dict(ms=best[0], gbs=(32 << 20) / (best[0] * 1e-3) / 1e9,
+                                     blocks=best[1], loads_in_flight=best[2],
+                                     what="one 32 MiB buffer per launch, 16 rotating, cold caches")
+    del bufs
     big = torch.randint(0, 256, (512 << 20,), dtype=torch.uint8, device=dev)
     best = None
     for blocks, unroll in ((2048, 4), (4096, 2), (1024, 8), (8192, 1)):
@@ -295,7 +307,8 @@ def main():
                                 frac_of_peak=mops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS)
     rows["ceilings"] = ceil
     log(f"ceilings: 4 MiB read {ceil['stream_read_4MiB']['ms']*1e3:.2f} us "
-        f"({ceil['stream_read_4MiB']['gbs']:.0f} GB/s), 512 MiB read "
+        f"({ceil['stream_read_4MiB']['gbs']:.0f} GB/s), 32 MiB read "
+        f"{ceil['stream_read_32MiB']['ms']*1e3:.2f} us ({ceil['stream_read_32MiB']['gbs']:.0f} GB/s), 512 MiB read "
         f"{ceil['stream_read_512MiB']['gbs']:.0f} GB/s, empty launch "
         f"{ceil['empty_launch_graph_us']:.2f} us, INT8 MFMA loop {ceil['mfma_i8_loop']['tops']:.0f} TOPS")
     torch.cuda.empty_cache()
@@ -317,7 +330,9 @@ def main():
             ms = graph_ms(f, 64)
             alg = pk.numel() + 2 * ps.K + 4 + 4 * ps.N
             rows[key] = dict(ms=ms, alg_bytes=alg, gbs=alg / (ms * 1e-3) / 1e9,
-                             frac_hbm=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                             frac_hbm=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             frac_of_32MiB_read=(alg / (ms * 1e-3) / 1e9)
+                             / ceil["stream_read_32MiB"]["gbs"])
             log(f"stream 32768x4096 {layout}: {ms*1e3:.2f} us = {alg/(ms*1e-3)/1e9:.0f} GB/s")
             del cps
         del Ws

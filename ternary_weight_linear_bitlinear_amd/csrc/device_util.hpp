@@ -178,6 +178,22 @@ __device__ __forceinline__ void expand_1bit_half(uint32_t w, int h, int out[4]) 
     }
 }
 
+// The same fields without the map to signed codes: dword j of out holds the
+// stored u = c + 1 (0, 1, 2) of codes 4j..4j+3 of a 2-bit word. A product
+// over u then differs from the product over c by the sum of the other
+// operand: sum_k u_k x_k = sum_k c_k x_k + sum_k x_k.
+__device__ __forceinline__ void fields_2bit_word(uint32_t w, int out[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = (int)((w >> (2 * j)) & 0x03030303u);
+}
+
+// 1-bit fields b = (c + 1) / 2 (0 or 1) of codes 16h + 4t .. +3, t = 0..3:
+// sum_k c_k x_k = 2 sum_k b_k x_k - sum_k x_k.
+__device__ __forceinline__ void fields_1bit_half(uint32_t w, int h, int out[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) out[t] = (int)((w >> (4 * h + t)) & 0x01010101u);
+}
+
 // Base-3 decode table: entry v (0..242) holds the five signed codes t_i - 1
 // of v = sum t_i 3^i in bytes 0..4 (bytes 5..7 zero); entries 243..255 are
 // zero. Built once per workgroup into LDS from this arithmetic definition.

@@ -75,19 +75,38 @@ __device__ __forceinline__ uint4 load_unit(const uint8_t *p) {
     }
 }
 
-// Decode one unit into signed code bytes (natural k order).
+// 2-bit and 1-bit units are multiplied as their stored fields (u = c + 1,
+// or b = (c + 1) / 2), two instructions per four codes instead of three; one
+// more matrix-core instruction per k-step, with every weight byte 1, gives
+// each wave the sum of the activations it multiplied, and the exact INT32
+// correction follows the last round: acc = sum u x - sum x (2-bit) or
+// 2 sum b x - sum x (1-bit). Base-3 units decode to signed codes through the
+// table. The correction's bound: each wave sums K / KS codes, so every
+// partial stays within 2 * 127 * K / KS (well inside INT32 for K < 2^31 / 127).
+template <int LAYOUT>
+constexpr bool kFieldCodes = LAYOUT != kLayoutBase3;
+constexpr int kOnes = 0x01010101;
+
+template <int LAYOUT>
+__device__ __forceinline__ v4i field_correction(const v4i acc, const v4i ones) {
+    if constexpr (LAYOUT == kLayout1Bit) return acc + acc - ones;
+    return acc - ones;
+}
+
+// Decode one unit into code bytes (natural k order): stored fields for 2-bit
+// and 1-bit (see above), signed codes for base-3.
 template <int LAYOUT>
 __device__ __forceinline__ void decode_unit(const uint4 wv, const uint64_t *lut, int c[20]) {
     if constexpr (LAYOUT == kLayout2Bit) {
-        expand_2bit_word(wv.x, c + 0);
-        expand_2bit_word(wv.y, c + 4);
-        expand_2bit_word(wv.z, c + 8);
-        expand_2bit_word(wv.w, c + 12);
+        fields_2bit_word(wv.x, c + 0);
+        fields_2bit_word(wv.y, c + 4);
+        fields_2bit_word(wv.z, c + 8);
+        fields_2bit_word(wv.w, c + 12);
     } else if constexpr (LAYOUT == kLayout1Bit) {
-        expand_1bit_half(wv.x, 0, c + 0);
-        expand_1bit_half(wv.x, 1, c + 4);
-        expand_1bit_half(wv.y, 0, c + 8);
-        expand_1bit_half(wv.y, 1, c + 12);
+        fields_1bit_half(wv.x, 0, c + 0);
+        fields_1bit_half(wv.x, 1, c + 4);
+        fields_1bit_half(wv.y, 0, c + 8);
+        fields_1bit_half(wv.y, 1, c + 12);
     } else {
         uint32_t d[20];
 #pragma unroll
@@ -225,6 +244,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     v4i acc[RG];
 #pragma unroll
     for (int q = 0; q < RG; ++q) acc[q] = v4i{0, 0, 0, 0};
+    v4i ones = {0, 0, 0, 0};  // field layouts: sum of the activations multiplied
 
     // every weight load of the round starting at unit u0. Out-of-range units
     // load a valid address and are used as loaded (see read_act_unit): a
@@ -273,6 +293,9 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
                                    c[q][4 * st + 3]};
                     acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[s][st], acc[q], 0, 0, 0);
                 }
+                if constexpr (kFieldCodes<LAYOUT>)
+                    ones = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{kOnes, kOnes, kOnes, kOnes},
+                                                                 b[s][st], ones, 0, 0, 0);
             }
         }
     };
@@ -354,6 +377,10 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
         }
     }
 
+    if constexpr (kFieldCodes<LAYOUT>) {
+#pragma unroll
+        for (int q = 0; q < RG; ++q) acc[q] = field_correction<LAYOUT>(acc[q], ones);
+    }
     lds_barrier();
 #pragma unroll
     for (int q = 0; q < RG; ++q) part[(q * KS + wave) * 64 + lane] = acc[q];
@@ -633,6 +660,7 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         v4i acc[RG];
 #pragma unroll
         for (int q = 0; q < RG; ++q) acc[q] = v4i{0, 0, 0, 0};
+        v4i ones = {0, 0, 0, 0};  // field layouts: sum of the activations multiplied
         for (int64_t u0 = 0; u0 < units; u0 += kRoundUnits) {
             if (!one_round) {
                 if (u0 > 0 || tile != tile0) {
@@ -666,6 +694,9 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
                         acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[st], acc[q], 0, 0,
                                                                        0);
                     }
+                    if constexpr (kFieldCodes<LAYOUT>)
+                        ones = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            v4i{kOnes, kOnes, kOnes, kOnes}, b[st], ones, 0, 0, 0);
                 }
             }
         }
@@ -684,6 +715,10 @@ __global__ __launch_bounds__(64 * KS) void linear_decode_kernel(
         // sum over the waves through LDS; two areas, so one barrier per tile
         // suffices (an area is rewritten only after the next tile's barrier,
         // which the reducing waves reach after their reads of this one)
+        if constexpr (kFieldCodes<LAYOUT>) {
+#pragma unroll
+            for (int q = 0; q < RG; ++q) acc[q] = field_correction<LAYOUT>(acc[q], ones);
+        }
         v4i *pb = part + buf * (RG * KS * 64);
         buf ^= 1;
 #pragma unroll

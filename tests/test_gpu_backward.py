@@ -223,3 +223,33 @@ def test_training_shapes_sampled(bl):
     ref = oracle.ste_grad_w(np.ascontiguousarray(p.grad_y[:, cols]), p.x)
     abs_sum = np.abs(p.grad_y[:, cols].astype(np.float64)).T @ np.abs(p.x.astype(np.float64))
     check_sum(gw[cols], ref, abs_sum, M, "grad_w rows")
+
+
+@pytest.mark.parametrize("variant", ["base3", "1bit", "fp32_grad_y"])
+def test_training_shapes_other_inputs(bl, variant):
+    """The benchmark's grad_x beside the training step, at 4096 x 4096 x 4096:
+    from the base-3 and 1-bit packed rows of the same weights, and from fp32
+    grad_y against the 2-bit rows. Sampled rows against the oracle (each a
+    full contraction of length 4096)."""
+    t = synth.workload("train")
+    M, N, K = t.M, t.N, t.K
+    banner(f"backward training shapes {variant} M={M} N={N} K={K}")
+    layout = {"base3": "base3", "1bit": "1bit", "fp32_grad_y": "2bit"}[variant]
+    scheme = "binary" if layout == "1bit" else "ternary"
+    packed, gamma = bl.bitlinear_pack_weights(dev(t.w_store, True), layout, scheme)
+    torch.cuda.synchronize()
+    codes, bad = oracle.unpack(to_np(packed), K, layout)
+    assert bad == 0
+    g = float(to_np(gamma)[0])
+    if variant == "fp32_grad_y":
+        gy = np.ascontiguousarray(t.grad_y, np.float32)  # bf16 values widened, as the benchmark does
+        gx = to_np(bl.bitlinear_backward_input(dev(gy), packed, gamma, K, layout))
+        n_terms = 3 * N
+    else:
+        gy = t.grad_y
+        gx = to_np(bl.bitlinear_backward_input(dev(t.grad_y_store, True), packed, gamma, K, layout))
+        n_terms = N
+    rows = np.sort(np.random.default_rng(6).choice(M, 6, replace=False))
+    ref = oracle.ste_grad_x(np.ascontiguousarray(gy[rows], np.float32), codes, g)
+    abs_sum = (np.abs(gy[rows].astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
+    check_sum(gx[rows], ref, abs_sum, n_terms, f"grad_x rows ({variant})")
