@@ -492,18 +492,21 @@ def main():
             tr[name + "_frac"] = tf / BF16_PEAK_TFLOPS
         tr["tokens_per_s"] = t.M / (tr["step_ms"] * 1e-3)
         # grad_x read from the other layouts' packed rows of the same weights,
-        # and from fp32 grad_y (three bf16 pieces); beside the step, not in it
+        # and from fp32 grad_y (three bf16 pieces); grad_W from fp32 operands
+        # (six piece products); beside the step, not in it
         var = {}
         for lay, sch in (("base3", "ternary"), ("1bit", "binary")):
             pk_l, g_l = bl.bitlinear_pack_weights(Wt, lay, sch)
             var[lay + "_ms"] = graph_ms(
                 lambda i: bl.bitlinear_backward_input(gyt, pk_l, g_l, t.K, lay, grad_x=gx_t), 10)
             del pk_l, g_l
-        gy32 = gyt.float()
+        gy32, x32 = gyt.float(), xt.float()
         var["fp32_grad_y_2bit_ms"] = graph_ms(
             lambda i: bl.bitlinear_backward_input(gy32, pk_t, g_t, t.K, grad_x=gx_t), 10)
-        del gy32
-        tr["backward_input_other_inputs"] = var
+        var["backward_weight_fp32_ms"] = graph_ms(
+            lambda i: bl.bitlinear_backward_weight(gy32, x32, grad_w=gw_t), 10)
+        del gy32, x32
+        tr["backward_other_inputs"] = var
         rows["train_step_4096"] = tr
         log(f"training step: {tr['step_ms']*1e3:.0f} us/step (fwd {tr['forward_int8_ms']*1e3:.0f}, "
             f"bwd in {tr['backward_input_bf16_ms']*1e3:.0f}, bwd w {tr['backward_weight_bf16_ms']*1e3:.0f} us)")

@@ -249,7 +249,13 @@ bl_status bitlinear_backward_input(const void *grad_y, int gy_dtype, const uint8
                                    int64_t K, float *grad_x, void *stream);
 
 /* bitlinear_backward_weight: grad_w[n,k] = sum_m grad_y[m,n] * x[m,k].
- *   grad_y  [M, N] bf16; x [M, K] bf16 (the layer input; dtype must be BL_BF16).
+ *   grad_y  [M, N]; x [M, K] (the layer input); both of `dtype`: BL_BF16
+ *           (products exact in fp32, fp32 sums), or BL_F32: each value is
+ *           split exactly into three bf16 pieces, and the six piece products
+ *           other than mid.lo, lo.mid and lo.lo are summed in fp32 (6M
+ *           terms), so each product is exact to within 2^-20 of its
+ *           magnitude (for values >= 2^-110; see backward_input). Six times
+ *           the matrix-core work of bf16.
  *   grad_w  out: [N, K] fp32.
  * Requires N % 8 == 0 and K % 8 == 0 (else BL_ERR_UNSUPPORTED). N = 0 is a
  * no-op; M = 0 writes zeros. */

@@ -271,15 +271,13 @@ bl_status bitlinear_backward_weight(const void *grad_y, const void *x, int dtype
     if (M < 0 || N < 0 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return BL_ERR_INVALID_ARG;
     if (!valid_dtype(dtype)) return BL_ERR_INVALID_ARG;
-    if (dtype != BL_BF16 || N % 8 != 0 || K % 8 != 0) return BL_ERR_UNSUPPORTED;
+    if (N % 8 != 0 || K % 8 != 0) return BL_ERR_UNSUPPORTED;
     if (N == 0) return BL_OK;
     bl_status st = device_ok();
     if (st != BL_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M == 0) return launched(bl::launch_zero_f32(grad_w, N * K, s));
-    return launched(bl::launch_backward_weight(static_cast<const uint16_t *>(grad_y),
-                                               static_cast<const uint16_t *>(x), M, N, K, grad_w,
-                                               s));
+    return launched(bl::launch_backward_weight(grad_y, x, dtype == BL_F32, M, N, K, grad_w, s));
 }
 
 int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int layout, int y_dtype, int fused,

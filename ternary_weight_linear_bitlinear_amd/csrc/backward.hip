@@ -131,15 +131,25 @@ __device__ __forceinline__ uint32_t f32_piece_bits(uint32_t ux, int piece) {
     return __float_as_uint(r - __uint_as_float(ur & 0xFFFF0000u));
 }
 
-// A_F32 (grad_x only): A holds fp32 values; the contraction runs three times
-// over p, once per bf16 piece of A (hi, mid, lo), into the same accumulators.
-template <bool A_T, int BSRC, bool A_F32 = false>
+// F32 = 1 (grad_x): A holds fp32 values; the contraction runs three times over
+// p, once per bf16 piece of A (hi, mid, lo), into the same accumulators.
+// F32 = 2 (grad_W): A and B hold fp32 values; six passes multiply the piece
+// pairs hi.hi, hi.mid, mid.hi, hi.lo, lo.hi and mid.mid. With |mid| < 2^-7 |x|
+// and |lo| < 2^-14 |x|, the three pairs left out (mid.lo, lo.mid, lo.lo) add
+// up to less than 2^-20 |a b|, so every product is exact to within 2^-20 of
+// its magnitude.
+constexpr int kPassesF32[3] = {1, 3, 6};
+constexpr int kPieceA6[6] = {0, 0, 1, 0, 2, 1}, kPieceB6[6] = {0, 1, 0, 2, 0, 1};
+
+template <bool A_T, int BSRC, int F32 = 0>
 __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
     const void *__restrict__ Av, int64_t lda, const void *__restrict__ Bv, int64_t ldb,
     int64_t I, int64_t J, int64_t P, const float *__restrict__ alpha_p, int tiles_i,
     int tiles_j, float *__restrict__ C, int64_t ldc) {
     using G = BwdCfg;
-    static_assert(!A_F32 || !A_T, "fp32 A only as stored [i][p]");
+    constexpr bool A_F32 = F32 >= 1, B_F32 = F32 == 2;
+    static_assert(F32 != 1 || !A_T, "fp32 A alone: grad_x, A stored [i][p]");
+    static_assert(F32 != 2 || (A_T && BSRC == kBDense), "fp32 A and B: grad_W");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint64_t *lut = reinterpret_cast<uint64_t *>(smem + G::SMEM);  // base-3 only
 
@@ -161,11 +171,13 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
     constexpr int A_W = A_F32 ? 2 : 1;  // 16-byte loads per chunk of 8 values
     v4i a_reg[A_CH][A_W];
     bool a_ok[A_CH];
-    v4i b_reg[B_CH];  // dense: 16-byte chunks; packed: one 8-byte piece in lanes 0, 1
+    constexpr int B_W = B_F32 ? 2 : 1;
+    v4i b_reg[B_CH][B_W];  // dense: 16-byte chunks (two for fp32); packed: one piece
     bool b_ok[B_CH];
     const uint16_t *A16 = static_cast<const uint16_t *>(Av);
     const float *A32 = static_cast<const float *>(Av);
     const uint16_t *B16 = static_cast<const uint16_t *>(Bv);
+    const float *B32 = static_cast<const float *>(Bv);
     const uint8_t *B8 = static_cast<const uint8_t *>(Bv);
 
     // Out-of-range pieces read a valid address and are zeroed when stored
@@ -199,7 +211,13 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                 const int q = tid + c * G::kThreads;
                 const int64_t p = p0 + q / (G::BJ / 8), j = j0 + 8 * (q % (G::BJ / 8));
                 b_ok[c] = p < P && j < J;
-                b_reg[c] = *reinterpret_cast<const v4i *>(B16 + (b_ok[c] ? p * ldb + j : 0));
+                if constexpr (B_F32) {
+                    const v4i *src = reinterpret_cast<const v4i *>(B32 + (b_ok[c] ? p * ldb + j : 0));
+                    b_reg[c][0] = src[0];
+                    b_reg[c][1] = src[1];
+                } else {
+                    b_reg[c][0] = *reinterpret_cast<const v4i *>(B16 + (b_ok[c] ? p * ldb + j : 0));
+                }
             }
         } else if constexpr (BSRC == kBPacked2) {
             // 64 rows x 64 packed bytes: 8 bytes (32 codes) per thread
@@ -207,14 +225,14 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
             const int64_t byte = j0 / 4 + 8 * (tid % 8);
             b_ok[0] = p < P && byte + 8 <= ldb;
             const uint2 v = *reinterpret_cast<const uint2 *>(B8 + (b_ok[0] ? p * ldb + byte : 0));
-            b_reg[0] = v4i{(int)v.x, (int)v.y, 0, 0};
+            b_reg[0][0] = v4i{(int)v.x, (int)v.y, 0, 0};
         } else if constexpr (BSRC == kBPacked1) {
             // 64 rows x 32 packed bytes: one 32-code word per thread
             const int64_t p = p0 + tid / 8;
             const int64_t byte = j0 / 8 + 4 * (tid % 8);
             b_ok[0] = p < P && byte + 4 <= ldb;
             const uint32_t v = *reinterpret_cast<const uint32_t *>(B8 + (b_ok[0] ? p * ldb + byte : 0));
-            b_reg[0] = v4i{(int)v, 0, 0, 0};
+            b_reg[0][0] = v4i{(int)v, 0, 0, 0};
         } else {
             // base-3: the eight bytes holding codes c0 .. c0 + 31 start at byte
             // b0 = c0 / 5, inside the three aligned dwords from b0 & ~3 (row
@@ -231,12 +249,13 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                 d[i] = row_ok && al + 4 * i < ldb ? row[al / 4 + i] : 0x79797979u;
             const uint32_t sh = (uint32_t)(b0 - al);
             b_ok[0] = row_ok;
-            b_reg[0] = v4i{(int)__builtin_amdgcn_alignbyte(d[1], d[0], sh),
+            b_reg[0][0] = v4i{(int)__builtin_amdgcn_alignbyte(d[1], d[0], sh),
                            (int)__builtin_amdgcn_alignbyte(d[2], d[1], sh), (int)(c0 - 5 * b0), 0};
         }
     };
 
-    auto store_stage = [&](uint8_t *st, int piece) __attribute__((always_inline)) {
+    // pass: which piece (pair) of fp32 operands this stage carries
+    auto store_stage = [&](uint8_t *st, int pass) __attribute__((always_inline)) {
         uint8_t *As = st;
         uint8_t *Bs = st + G::A_BYTES;
         const v4i z = {0, 0, 0, 0};
@@ -247,9 +266,10 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                                  : (q / (G::BI / 8)) * G::LD_PX + 16 * (q % (G::BI / 8));
             v4i v;
             if constexpr (A_F32) {
+                const int pa = B_F32 ? kPieceA6[pass] : pass;
                 uint32_t h[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) h[e] = f32_piece_bits((uint32_t)a_reg[c][e / 4][e % 4], piece);
+                for (int e = 0; e < 8; ++e) h[e] = f32_piece_bits((uint32_t)a_reg[c][e / 4][e % 4], pa);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = (int)top_halves(h[2 * e], h[2 * e + 1]);
             } else {
@@ -262,12 +282,23 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
             for (int c = 0; c < B_CH; ++c) {
                 const int q = tid + c * G::kThreads;
                 const int off = (q / (G::BJ / 8)) * G::LD_PX + 16 * (q % (G::BJ / 8));
-                *reinterpret_cast<v4i *>(Bs + off) = b_ok[c] ? b_reg[c] : z;
+                v4i v;
+                if constexpr (B_F32) {
+                    const int pb = kPieceB6[pass];
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[e] = f32_piece_bits((uint32_t)b_reg[c][e / 4][e % 4], pb);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (int)top_halves(h[2 * e], h[2 * e + 1]);
+                } else {
+                    v = b_reg[c][0];
+                }
+                *reinterpret_cast<v4i *>(Bs + off) = b_ok[c] ? v : z;
             }
         } else if constexpr (BSRC == kBPacked1) {
             // bit t of byte i of the word is code 4 t + i; u = 2 bit (0 or 2)
             // picks -1 or +1. Rows past P multiply zeros of A.
-            const uint32_t word = (uint32_t)b_reg[0][0];
+            const uint32_t word = (uint32_t)b_reg[0][0][0];
             uint8_t *dst = Bs + (tid / 8) * G::LD_PX + 64 * (tid % 8);
             uint32_t d[16];
 #pragma unroll
@@ -279,7 +310,7 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
                     make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
         } else if constexpr (BSRC == kBPacked3) {
             uint32_t f[8];
-            base3_fields((uint32_t)b_reg[0][0], (uint32_t)b_reg[0][1], b_reg[0][2], lut, f);
+            base3_fields((uint32_t)b_reg[0][0][0], (uint32_t)b_reg[0][0][1], b_reg[0][0][2], lut, f);
             uint8_t *dst = Bs + (tid / 8) * G::LD_PX + 64 * (tid % 8);
             uint32_t d[16];
 #pragma unroll
@@ -291,8 +322,8 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
         } else {
             // word w holds codes 16 w .. 16 w + 15 of the piece; field s of a
             // word holds its codes 4 s .. 4 s + 3 (one per byte)
-            const uint32_t words[2] = {b_ok[0] ? (uint32_t)b_reg[0][0] : 0x55555555u,
-                                       b_ok[0] ? (uint32_t)b_reg[0][1] : 0x55555555u};
+            const uint32_t words[2] = {b_ok[0] ? (uint32_t)b_reg[0][0][0] : 0x55555555u,
+                                       b_ok[0] ? (uint32_t)b_reg[0][0][1] : 0x55555555u};
             uint8_t *dst = Bs + (tid / 8) * G::LD_PX + 64 * (tid % 8);
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
@@ -359,11 +390,12 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
         if (tid < 256) lut[tid] = base3_field_entry((uint32_t)tid);
         __syncthreads();
     }
-    // stage s: contraction slice s % per_piece, piece s / per_piece of fp32 A
-    const int64_t per_piece = (P + G::BP - 1) / G::BP;
-    const int64_t nst = per_piece * (A_F32 ? 3 : 1);
-    auto slice_of = [&](int64_t s) { return (A_F32 ? s % per_piece : s) * G::BP; };
-    auto piece_of = [&](int64_t s) { return A_F32 ? (int)(s / per_piece) : 0; };
+    // stage s: contraction slice s % per_pass of pass s / per_pass (fp32
+    // operands: one pass per piece or piece pair)
+    const int64_t per_pass = (P + G::BP - 1) / G::BP;
+    const int64_t nst = per_pass * kPassesF32[F32];
+    auto slice_of = [&](int64_t s) { return (F32 ? s % per_pass : s) * G::BP; };
+    auto piece_of = [&](int64_t s) { return F32 ? (int)(s / per_pass) : 0; };
     load_stage(0);
     store_stage(smem, 0);
     __syncthreads();
@@ -392,14 +424,14 @@ __global__ __launch_bounds__(BwdCfg::kThreads) void bwd_gemm_kernel(
         }
 }
 
-template <bool A_T, int BSRC, bool A_F32 = false>
+template <bool A_T, int BSRC, int F32 = 0>
 hipError_t launch_bwd(const void *A, int64_t lda, const void *B, int64_t ldb, int64_t I,
                       int64_t J, int64_t P, const float *alpha, float *C, int64_t ldc,
                       hipStream_t s) {
     using G = BwdCfg;
     const int ti = (int)((I + G::BI - 1) / G::BI), tj = (int)((J + G::BJ - 1) / G::BJ);
     const int64_t blocks = ((int64_t)ti * tj + kXcds - 1) / kXcds * kXcds;
-    auto kern = bwd_gemm_kernel<A_T, BSRC, A_F32>;
+    auto kern = bwd_gemm_kernel<A_T, BSRC, F32>;
     const int smem = G::SMEM + (BSRC == kBPacked3 ? G::LUT3 : 0);
     static LdsFlag lds_raised{0};
     hipError_t e = allow_dynamic_lds(kern, smem, &lds_raised);
@@ -425,7 +457,7 @@ hipError_t launch_zero_f32(float *out, int64_t count, hipStream_t stream) {
 }
 
 namespace {
-template <bool F32>
+template <int F32>
 hipError_t backward_input_t(const void *grad_y, const uint8_t *packed, int layout,
                             const float *gamma, int64_t M, int64_t N, int64_t K, float *grad_x,
                             hipStream_t stream) {
@@ -443,13 +475,13 @@ hipError_t backward_input_t(const void *grad_y, const uint8_t *packed, int layou
 hipError_t launch_backward_input(const void *grad_y, bool grad_y_f32, const uint8_t *packed,
                                  int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                                  float *grad_x, hipStream_t stream) {
-    return grad_y_f32 ? backward_input_t<true>(grad_y, packed, layout, gamma, M, N, K, grad_x, stream)
-                      : backward_input_t<false>(grad_y, packed, layout, gamma, M, N, K, grad_x,
-                                                stream);
+    return grad_y_f32 ? backward_input_t<1>(grad_y, packed, layout, gamma, M, N, K, grad_x, stream)
+                      : backward_input_t<0>(grad_y, packed, layout, gamma, M, N, K, grad_x, stream);
 }
 
-hipError_t launch_backward_weight(const uint16_t *grad_y, const uint16_t *x, int64_t M, int64_t N,
-                                  int64_t K, float *grad_w, hipStream_t stream) {
+hipError_t launch_backward_weight(const void *grad_y, const void *x, bool f32, int64_t M,
+                                  int64_t N, int64_t K, float *grad_w, hipStream_t stream) {
+    if (f32) return launch_bwd<true, kBDense, 2>(grad_y, N, x, K, N, K, M, nullptr, grad_w, K, stream);
     return launch_bwd<true, kBDense>(grad_y, N, x, K, N, K, M, nullptr, grad_w, K, stream);
 }
 

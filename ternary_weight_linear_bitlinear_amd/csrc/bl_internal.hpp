@@ -179,8 +179,8 @@ hipError_t launch_forward_lut(const int8_t *xq, const float *scale, const uint8_
 hipError_t launch_backward_input(const void *grad_y, bool grad_y_f32, const uint8_t *packed,
                                  int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                                  float *grad_x, hipStream_t stream);
-// grad_w [N, K] fp32 = grad_y^T (bf16 [M, N]) x x (bf16 [M, K]).
-hipError_t launch_backward_weight(const uint16_t *grad_y, const uint16_t *x, int64_t M,
+// grad_w [N, K] fp32 = grad_y^T ([M, N]) x x ([M, K]), both bf16, or both fp32 when f32.
+hipError_t launch_backward_weight(const void *grad_y, const void *x, bool f32, int64_t M,
                                   int64_t N, int64_t K, float *grad_w, hipStream_t stream);
 // out[0 : count) = 0 (a kernel, so it can be captured in a graph).
 hipError_t launch_zero_f32(float *out, int64_t count, hipStream_t stream);

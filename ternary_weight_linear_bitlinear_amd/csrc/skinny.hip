@@ -1,7 +1,9 @@
 // Decode-side product for small batches (1 <= M <= 16 tokens): the packed
 // weights are streamed from HBM exactly once with 16-byte loads, expanded in
-// registers to signed code bytes, and multiplied on the INT8 matrix cores
-// (v_mfma_i32_16x16x64_i8) with the batch in the 16-column operand. A
+// registers to code bytes (the stored 2-bit / 1-bit fields, corrected
+// exactly afterwards; signed codes for base-3), and multiplied on the INT8
+// matrix cores (v_mfma_i32_16x16x64_i8) with the batch in the 16-column
+// operand. A
 // weight of +1 adds the activation, -1 subtracts it and 0 contributes
 // nothing ([b158] "BitNet b1.58深度解析" §4.2); the sums are exact INT32
 // ([b158] §3.3), then scaled by gamma * scale[m] / 127 ([b158] §5.2-5.3).

@@ -167,7 +167,7 @@ def test_backward_rejects_and_limits(bl):
     assert bw(gw=P + 8) == bl.BL_ERR_INVALID_ARG
     assert bw(K=0) == bl.BL_ERR_INVALID_ARG
     assert bw(dt=3) == bl.BL_ERR_INVALID_ARG
-    assert bw(dt=0) == bl.BL_ERR_UNSUPPORTED
+    assert bw(dt=0, K=60) == bl.BL_ERR_UNSUPPORTED
     assert bw(K=60) == bl.BL_ERR_UNSUPPORTED
     assert bw(N=12) == bl.BL_ERR_UNSUPPORTED
     assert bw(N=0) == bl.BL_OK

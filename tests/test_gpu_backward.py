@@ -97,6 +97,43 @@ def test_backward_weight_parity(bl, M, N, K):
     check_sum(to_np(gw), ref, abs_sum, M, "grad_w")
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 520, 264), (33, 8, 1000), (17, 264, 2056),
+                                   (6, 16, 24)])
+def test_backward_weight_fp32(bl, M, N, K):
+    """fp32 grad_y and x: six piece products per term, summed in fp32 (6M
+    terms), with the three dropped pairs under 2^-20 (= 16 u) of each
+    product: bound (6M + 16) u per unit of the sum of |terms|. At M = 6 that
+    is ~3e-6 of it, against 2^-14 for a lost lo piece or a lost pair."""
+    banner(f"backward_weight fp32 M={M} N={N} K={K}")
+    p = synth.make_problem(M=M, N=N, K=K, seed=700 + M + N + K, dtype="f32", grad_std=1e-3)
+    gy = np.ascontiguousarray(p.grad_y, np.float32)
+    x = np.ascontiguousarray(p.x, np.float32)
+    gw = to_np(bl.bitlinear_backward_weight(dev(gy), dev(x)))
+    ref = oracle.ste_grad_w(gy, x)
+    abs_sum = np.abs(gy.astype(np.float64)).T @ np.abs(x.astype(np.float64))
+    check_sum(gw, ref, abs_sum, 6 * M + 16, "grad_w fp32")
+
+
+def test_backward_weight_fp32_wide_range(bl):
+    """Both operands with full 24-bit significands over exponents 2^-50 .. 2^20
+    and both signs (products stay far from fp32's range limits)."""
+    M, N, K = 8, 64, 96
+    banner(f"backward_weight fp32 wide range M={M} N={N} K={K}")
+    rng = np.random.default_rng(13)
+
+    def wide(shape):
+        mant = 1.0 + rng.integers(0, 1 << 23, size=shape) / float(1 << 23)
+        expo = rng.integers(-50, 21, size=shape)
+        sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+        return (sign * mant * np.exp2(expo)).astype(np.float32)
+
+    gy, x = wide((M, N)), wide((M, K))
+    gw = to_np(bl.bitlinear_backward_weight(dev(gy), dev(x)))
+    ref = oracle.ste_grad_w(gy, x)
+    abs_sum = np.abs(gy.astype(np.float64)).T @ np.abs(x.astype(np.float64))
+    check_sum(gw, ref, abs_sum, 6 * M + 16, "grad_w fp32 wide range")
+
+
 @pytest.mark.parametrize("layout", ["2bit", "base3", "1bit"])
 @pytest.mark.parametrize("K", [1001, 5, 255, 261, 1281])
 def test_backward_input_ragged_k(bl, layout, K):
@@ -253,3 +290,18 @@ def test_training_shapes_other_inputs(bl, variant):
     ref = oracle.ste_grad_x(np.ascontiguousarray(gy[rows], np.float32), codes, g)
     abs_sum = (np.abs(gy[rows].astype(np.float64)) @ np.abs(codes.astype(np.float64))) * g
     check_sum(gx[rows], ref, abs_sum, n_terms, f"grad_x rows ({variant})")
+
+
+def test_training_shapes_weight_fp32(bl):
+    """The benchmark's fp32 grad_W beside the training step (bf16 grad_y and x
+    widened to fp32, 4096 x 4096 x 4096): sampled rows of grad_W."""
+    t = synth.workload("train")
+    M, N, K = t.M, t.N, t.K
+    banner(f"backward_weight fp32 training shapes M={M} N={N} K={K}")
+    gy = np.ascontiguousarray(t.grad_y, np.float32)
+    x = np.ascontiguousarray(t.x, np.float32)
+    gw = to_np(bl.bitlinear_backward_weight(dev(gy), dev(x)))
+    cols = np.sort(np.random.default_rng(7).choice(N, 6, replace=False))
+    ref = oracle.ste_grad_w(np.ascontiguousarray(gy[:, cols]), x)
+    abs_sum = np.abs(gy[:, cols].astype(np.float64)).T @ np.abs(x.astype(np.float64))
+    check_sum(gw[cols], ref, abs_sum, 6 * M + 16, "grad_w fp32 rows")
