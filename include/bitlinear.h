@@ -228,7 +228,8 @@ bl_status bitlinear_forward_lut(const int8_t *xq, const float *scale, const uint
  * reach the latent weights; [b158] §5.3, the BitLinear layer with the
  * straight-through estimator). With y = x W_q^T and W_q = gamma * c:
  *   grad_x = grad_y W_q   and   grad_W = grad_y^T x.
- * Both run on the bf16 matrix cores with fp32 accumulation.
+ * Both run on the bf16 matrix cores with fp32 accumulation (fp32 operands
+ * as exact bf16 pieces, below).
  *
  * bitlinear_backward_input: grad_x[m,k] = gamma * sum_n grad_y[m,n] * c[n,k].
  *   grad_y  [M, N], gy_dtype BL_BF16 or BL_F32. fp32 values are split exactly

@@ -241,6 +241,13 @@ def test_backward_empty_sums_write_zeros(bl):
     assert lib.bitlinear_backward_weight(P(dummy), P(dummy), 1, 0, 16, 24, P(gw), s) == 0
     torch.cuda.synchronize()
     assert not gx.any() and not gw.any()
+    # the same with fp32 operands
+    gx.fill_(7.0)
+    gw.fill_(7.0)
+    assert lib.bitlinear_backward_input(P(dummy), 0, P(packed), 0, P(gamma), 5, 0, 24, P(gx), s) == 0
+    assert lib.bitlinear_backward_weight(P(dummy), P(dummy), 0, 0, 16, 24, P(gw), s) == 0
+    torch.cuda.synchronize()
+    assert not gx.any() and not gw.any()
 
 
 def test_training_shapes_sampled(bl):
