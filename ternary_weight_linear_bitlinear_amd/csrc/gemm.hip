@@ -67,7 +67,10 @@ struct GemmCfg {
     // each k-group stages its own tiles; afterwards groups 1..KG-1 hand their
     // INT32 tile to group 0 through the same memory
     static constexpr int STAGES = KG * 2 * STAGE, RED = (KG - 1) * BM * BN * 4;
-    static constexpr int SMEM = LUT + (STAGES > RED ? STAGES : RED);
+    // bf16 tiles leave through LDS one row of waves at a time (BM / WM rows)
+    static constexpr int OUT = (BM / WM) * (BN * 2 + 16);
+    static constexpr int SMEM0 = STAGES > RED ? STAGES : RED;
+    static constexpr int SMEM = LUT + (SMEM0 > OUT ? SMEM0 : OUT);
     static_assert(BM * BK % (16 * kGroupThreads) == 0, "A tile must split evenly");
     static_assert(DIST == 1 || DIST == 2 || DIST == 4, "register sets: 1, 2 or 4");
 };
@@ -627,7 +630,7 @@ __global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, i
     const int b = blockIdx.x;
     if (b < blocks1) {
         const int t = xcd_tile(b, g1.tiles_m * g1.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 2, 4, 2, 1, KMODE, YT>(g1, t);
+        if (t >= 0) gemm_tile<LAYOUT, 256, 256, 1, 8, 2, 1, KMODE, YT>(g1, t);
     } else {
         const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
         if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, 1, KMODE, YT>(g2, t);
@@ -749,9 +752,9 @@ template <int LAYOUT, typename YT>
 hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t n_main,
                             YT *y, int32_t *acc, hipStream_t s) {
-    using C1 = GemmCfg<LAYOUT, 256, 256, 2, 4, 2>;
+    using C1 = GemmCfg<LAYOUT, 256, 256, 1, 8, 2>;
     using C2 = GemmCfg<LAYOUT, 256, 128, 2, 4, 2>;
-    static_assert(C1::SMEM == C2::SMEM && C1::kThreads == C2::kThreads, "one launch shape");
+    static_assert(C1::SMEM >= C2::SMEM && C1::kThreads == C2::kThreads, "one launch shape");
     const int64_t rb = row_bytes_of(LAYOUT, K);
     const int tm = (int)((M + 255) / 256);
     const int tn1 = (int)((n_main + 255) / 256), tn2 = (int)((N - n_main + 127) / 128);
@@ -807,7 +810,7 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
             if (n_rest > 0 && t_rest >= 128 && t_rest <= kCUs)
                 return launch_gemm_pair<LAYOUT>(xq, scale, packed, gamma, M, N, K, n_main, y, acc,
                                                 s);
-            hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 2, 4, 2>(
+            hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 1, 8, 2>(
                 xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
             if (e != hipSuccess || n_main == N) return e;
             return launch_gemm_cols<LAYOUT>(xq, scale, packed + n_main * rb,
