@@ -248,11 +248,11 @@ def test_forward_long_rows_sampled(bl, layout):
 
 @pytest.mark.parametrize("layout,M,N,K,kernel", [
     # one round of 128 x 128 tiles, one wave group, whole k-tiles
-    ("2bit", 1000, 4096, 4096, "gemm_kernel<0, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
-    ("1bit", 1000, 4096, 4096, "gemm_kernel<2, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
+    ("2bit", 1000, 4096, 4096, "gemm_kernel<0, 128, 128, 1, 4, 2, 1, 0, unsigned short>"),
+    ("1bit", 1000, 4096, 4096, "gemm_kernel<2, 128, 128, 1, 4, 2, 1, 0, unsigned short>"),
     # many row tiles over one column of tiles, not a whole number of rounds
-    ("2bit", 70000, 200, 256, "gemm_kernel<0, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
-    ("1bit", 70000, 200, 256, "gemm_kernel<2, 128, 128, 2, 2, 2, 1, 0, unsigned short>"),
+    ("2bit", 70000, 200, 256, "gemm_kernel<0, 128, 128, 1, 4, 2, 1, 0, unsigned short>"),
+    ("1bit", 70000, 200, 256, "gemm_kernel<2, 128, 128, 1, 4, 2, 1, 0, unsigned short>"),
     ("base3", 70000, 200, 256, "gemm_kernel<1, 256, 128, 2, 4, 2, 1, 0, unsigned short>"),
 ])
 def test_forward_large_sampled(bl, layout, M, N, K, kernel):
