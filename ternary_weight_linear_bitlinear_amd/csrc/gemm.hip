@@ -633,7 +633,7 @@ __global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, i
         if (t >= 0) gemm_tile<LAYOUT, 256, 256, 1, 8, 2, 1, KMODE, YT>(g1, t);
     } else {
         const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 256, 128, 2, 4, 2, 1, KMODE, YT>(g2, t);
+        if (t >= 0) gemm_tile<LAYOUT, 128, 256, 1, 8, 2, 1, KMODE, YT>(g2, t);
     }
 }
 
@@ -704,10 +704,18 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     // exactly half, one round of 128 x 128 tiles is faster), and, except for
     // base-3 (whose weight decode the 256 tokens of a tile share), their last
     // row of tiles is at least three quarters full (384 tokens: 128-row tiles
-    // are faster)
+    // are faster). 2-bit and 1-bit take the same area as 128 x 256 tiles, one
+    // row of eight waves of 128 x 32, so that each code is expanded by one wave
+    // only (512 x 12288 x 4096: 36.9 -> 33.4 us); base-3's 160-code k-tile does
+    // not split evenly over 128 rows of eight waves.
     const bool rows_fill = LAYOUT == kLayoutBase3 || M % 256 == 0 || M % 256 >= 192;
-    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)))
-        BL_GEMM_TILE(256, 128, 2, 4, 2);
+    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256))) {
+        if constexpr (LAYOUT != kLayoutBase3) {
+            BL_GEMM_TILE(128, 256, 1, 8, 2);
+        } else {
+            BL_GEMM_TILE(256, 128, 2, 4, 2);
+        }
+    }
     if (long_k) {
         if constexpr (LAYOUT != kLayoutBase3) {
             // at most half a round of 128 x 64 tiles: 64 x 64 tiles, also
@@ -746,25 +754,25 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
 #undef BL_GEMM_TILE
 }
 
-// Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in 256 x 128 tiles,
+// Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in 128 x 256 tiles,
 // one launch (2-bit and 1-bit).
 template <int LAYOUT, typename YT>
 hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t n_main,
                             YT *y, int32_t *acc, hipStream_t s) {
     using C1 = GemmCfg<LAYOUT, 256, 256, 1, 8, 2>;
-    using C2 = GemmCfg<LAYOUT, 256, 128, 2, 4, 2>;
+    using C2 = GemmCfg<LAYOUT, 128, 256, 1, 8, 2>;
     static_assert(C1::SMEM >= C2::SMEM && C1::kThreads == C2::kThreads, "one launch shape");
     const int64_t rb = row_bytes_of(LAYOUT, K);
-    const int tm = (int)((M + 255) / 256);
-    const int tn1 = (int)((n_main + 255) / 256), tn2 = (int)((N - n_main + 127) / 128);
+    const int tm = (int)((M + 255) / 256), tm2 = (int)((M + 127) / 128);
+    const int tn1 = (int)((n_main + 255) / 256), tn2 = (int)((N - n_main + 255) / 256);
     GemmArgs<YT> g1{xq, scale, packed, gamma, M, n_main, K, rb, tm, tn1, y, N, acc};
     GemmArgs<YT> g2{xq, scale, packed + n_main * rb, gamma.from_row(n_main), M, N - n_main,
-                    K, rb, tm, tn2, y + n_main, N, acc ? acc + n_main : nullptr};
+                    K, rb, tm2, tn2, y + n_main, N, acc ? acc + n_main : nullptr};
     g1.band = tile_band(tm, tn1, 256 * K, 256 * rb);
-    g2.band = tile_band(tm, tn2, 256 * K, 128 * rb);
+    g2.band = tile_band(tm2, tn2, 128 * K, 256 * rb);
     const int blocks1 = (tm * tn1 + kXcds - 1) / kXcds * kXcds;
-    const int blocks2 = (tm * tn2 + kXcds - 1) / kXcds * kXcds;
+    const int blocks2 = (tm2 * tn2 + kXcds - 1) / kXcds * kXcds;
     auto launch = [&](auto kern, LdsFlag *flag) {
         hipError_t e = allow_dynamic_lds(kern, C1::SMEM, flag);
         if (e != hipSuccess) return e;
@@ -774,8 +782,8 @@ hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t 
     };
     if (t_plan) {
         plan_note((unsigned)(blocks1 + blocks2), 1, C1::kThreads, C1::SMEM,
-                  "gemm_pair_kernel<%d, %d, %s> (%d tiles 256x256 + %d tiles 256x128)", LAYOUT,
-                  gemm_k_mode(LAYOUT, K), type_name<YT>(), tm * tn1, tm * tn2);
+                  "gemm_pair_kernel<%d, %d, %s> (%d tiles 256x256 + %d tiles 128x256)", LAYOUT,
+                  gemm_k_mode(LAYOUT, K), type_name<YT>(), tm * tn1, tm2 * tn2);
         return hipSuccess;
     }
     static LdsFlag lds_flag[3];  // one per k-mode
@@ -806,7 +814,7 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
                 return launch_gemm_cols<LAYOUT>(xq, scale, packed, gamma, M, N, K, y, N, acc, s);
             const int64_t n_main = tn_main * 256 < N ? tn_main * 256 : N;
             const int64_t n_rest = N - n_main;
-            const int64_t t_rest = tm * ((n_rest + 127) / 128);
+            const int64_t t_rest = ((M + 127) / 128) * ((n_rest + 255) / 256);
             if (n_rest > 0 && t_rest >= 128 && t_rest <= kCUs)
                 return launch_gemm_pair<LAYOUT>(xq, scale, packed, gamma, M, N, K, n_main, y, acc,
                                                 s);

@@ -184,9 +184,9 @@ def test_bench_weight_stream_32768(bl, layout):
 
 # --------------------------------------------------------------- prefill, C3
 @pytest.mark.parametrize("layout,kernel", [
-    ("2bit", "gemm_pair_kernel<0, 0, unsigned short> (256 tiles 256x256 + 176 tiles 256x128)"),
+    ("2bit", "gemm_pair_kernel<0, 0, unsigned short> (256 tiles 256x256 + 176 tiles 128x256)"),
     ("base3", "gemm_kernel<1, 256, 128, 2, 4, 2, 1, 0, unsigned short>"),
-    ("1bit", "gemm_pair_kernel<2, 0, unsigned short> (256 tiles 256x256 + 176 tiles 256x128)"),
+    ("1bit", "gemm_pair_kernel<2, 0, unsigned short> (256 tiles 256x256 + 176 tiles 128x256)"),
 ])
 def test_bench_prefill(bl, layout, kernel):
     p = synth.workload("prefill")
@@ -207,9 +207,9 @@ BLOCK_16 = {
     "down": "skinny_kernel<0, 8, 2, 1, 16, true, unsigned short>",
 }
 BLOCK_512 = {
-    "qkv": "gemm_kernel<0, 256, 128, 2, 4, 2, 1, 0, unsigned short>",
+    "qkv": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",
     "o": "gemm_kernel<0, 64, 64, 2, 2, 2, 1, 0, unsigned short>",
-    "up": "gemm_kernel<0, 256, 128, 2, 4, 2, 1, 0, unsigned short>",
+    "up": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",
     "down": "gemm_kernel<0, 128, 64, 2, 2, 2, 2, 0, unsigned short>",
 }
 
