@@ -698,6 +698,21 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
 #define BL_GEMM_TILE(...)                                                                    \
     return launch_gemm_tile<LAYOUT, __VA_ARGS__>(xq, scale, packed, gamma, M, N, K, y, ldy, acc, \
                                                  s)
+    // 2-bit and 1-bit run the narrow tiles with the same area as one row of
+    // four waves, so each code is expanded by one wave only: 64 x 128 in place
+    // of 128 x 64 (512 x 4096 x 11008 with split k-tiles: 40.6 -> 35.5 us) and
+    // 32 x 128 in place of 64 x 64 (256 x 4096 x 4096: 14.0 -> 13.5 us).
+    // Base-3 keeps two rows of waves (its 160-code k-tile does not split
+    // evenly over fewer rows).
+#define BL_TILE_128x64(...)                                                                  \
+    do {                                                                                     \
+        if constexpr (LAYOUT != kLayoutBase3) {                                              \
+            BL_GEMM_TILE(64, 128, 1, 4, 2 __VA_ARGS__);                                      \
+        } else {                                                                             \
+            BL_GEMM_TILE(128, 64, 2, 2, 2 __VA_ARGS__);                                      \
+        }                                                                                    \
+    } while (0)
+#define BL_TILE_64x64(...) BL_GEMM_TILE(32, 128, 1, 4, 2 __VA_ARGS__)
     // 256 x 128 tiles when they make several rounds, or one round that keeps
     // more than half of the 256 CUs busy (measured faster than two rounds of
     // 128 x 128 tiles for the leftover columns of the prefill shape; at
@@ -721,9 +736,9 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
             // at most half a round of 128 x 64 tiles: 64 x 64 tiles, also
             // with split k-tiles, reach twice the CUs (256 x 4096 x 11008:
             // 37.2 -> 25.7 us)
-            if (t_small <= 128 && tiles(64, 64) <= 256) BL_GEMM_TILE(64, 64, 2, 2, 2, 2);
+            if (t_small <= 128 && tiles(64, 64) <= 256) BL_TILE_64x64(, 2);
         }
-        if (t_small <= 256) BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
+        if (t_small <= 256) BL_TILE_128x64(, 2);
         if (t_sq >= 160) BL_GEMM_TILE(128, 128, 1, 4, 2, 2);
     }
     // base-3, at most half a round of 128 x 64 tiles over split_kt or more
@@ -747,10 +762,12 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
         // each tile's k-tiles (192 x 3000 x 5000: 36.1 -> 29.4 us, 320 x 2048
         // x 8000: 24.7 -> 20.3 us; over more than one round the split was
         // 7-9% slower)
-        if (ktiles >= split_kt && tiles(64, 64) <= 256) BL_GEMM_TILE(64, 64, 2, 2, 2, 2);
-        if (t_small <= 384) BL_GEMM_TILE(64, 64, 2, 2, 2);
+        if (ktiles >= split_kt && tiles(64, 64) <= 256) BL_TILE_64x64(, 2);
+        if (t_small <= 384) BL_TILE_64x64();
     }
-    BL_GEMM_TILE(128, 64, 2, 2, 2);
+    BL_TILE_128x64();
+#undef BL_TILE_64x64
+#undef BL_TILE_128x64
 #undef BL_GEMM_TILE
 }
 

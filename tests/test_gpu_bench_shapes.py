@@ -208,9 +208,9 @@ BLOCK_16 = {
 }
 BLOCK_512 = {
     "qkv": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",
-    "o": "gemm_kernel<0, 64, 64, 2, 2, 2, 1, 0, unsigned short>",
+    "o": "gemm_kernel<0, 32, 128, 1, 4, 2, 1, 0, unsigned short>",
     "up": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",
-    "down": "gemm_kernel<0, 128, 64, 2, 2, 2, 2, 0, unsigned short>",
+    "down": "gemm_kernel<0, 64, 128, 1, 4, 2, 2, 0, unsigned short>",
 }
 
 
