@@ -60,7 +60,12 @@ struct GemmCfg {
     static constexpr int BK = 2 * UC;                             // codes per k-tile
     static constexpr int LDSK = BK + 16;                          // padded LDS row (bytes)
     static constexpr int KSTEPS = UC / 16;                        // MFMA k-steps per tile
-    static constexpr int ACH = BM * BK / 16 / kGroupThreads;      // A 16B chunks per thread
+    // A tile in 16-byte chunks, dealt round-robin over the group's threads;
+    // when they do not divide evenly the last chunk slot of some threads is
+    // empty (base-3's 160-code k-tile over one row of waves)
+    static constexpr int ACHUNKS = BM * BK / 16;
+    static constexpr int ACH = (ACHUNKS + kGroupThreads - 1) / kGroupThreads;
+    static constexpr bool A_EVEN = ACHUNKS % kGroupThreads == 0;
     static constexpr int FI = BM / WM / 32, FJ = BN / WN / 32;    // fragments per wave
     static constexpr int STAGE = BM * LDSK;
     static constexpr int LUT = LAYOUT == kLayoutBase3 ? 8192 : 0;
@@ -71,7 +76,6 @@ struct GemmCfg {
     static constexpr int OUT = (BM / WM) * (BN * 2 + 16);
     static constexpr int SMEM0 = STAGES > RED ? STAGES : RED;
     static constexpr int SMEM = LUT + (SMEM0 > OUT ? SMEM0 : OUT);
-    static_assert(BM * BK % (16 * kGroupThreads) == 0, "A tile must split evenly");
     static_assert(DIST == 1 || DIST == 2 || DIST == 4, "register sets: 1, 2 or 4");
 };
 
@@ -244,6 +248,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
             const int q = gtid + i * kGT;
+            if (!C::A_EVEN && i == C::ACH - 1 && q >= C::ACHUNKS) continue;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             const int64_t m = m0 + row, k = kc0 + col * 16;
             if (!G || EVEN_K) {
@@ -293,6 +298,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs<YT> &g, int t) {
 #pragma unroll
         for (int i = 0; i < C::ACH; ++i) {
             const int q = gtid + i * kGT;
+            if (!C::A_EVEN && i == C::ACH - 1 && q >= C::ACHUNKS) continue;
             const int row = q / (C::BK / 16), col = q % (C::BK / 16);
             v4i v = a_reg[i];
             const int64_t kb = kt * C::BK + col * 16;
@@ -698,20 +704,12 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
 #define BL_GEMM_TILE(...)                                                                    \
     return launch_gemm_tile<LAYOUT, __VA_ARGS__>(xq, scale, packed, gamma, M, N, K, y, ldy, acc, \
                                                  s)
-    // 2-bit and 1-bit run the narrow tiles with the same area as one row of
-    // four waves, so each code is expanded by one wave only: 64 x 128 in place
-    // of 128 x 64 (512 x 4096 x 11008 with split k-tiles: 40.6 -> 35.5 us) and
-    // 32 x 128 in place of 64 x 64 (256 x 4096 x 4096: 14.0 -> 13.5 us).
-    // Base-3 keeps two rows of waves (its 160-code k-tile does not split
-    // evenly over fewer rows).
-#define BL_TILE_128x64(...)                                                                  \
-    do {                                                                                     \
-        if constexpr (LAYOUT != kLayoutBase3) {                                              \
-            BL_GEMM_TILE(64, 128, 1, 4, 2 __VA_ARGS__);                                      \
-        } else {                                                                             \
-            BL_GEMM_TILE(128, 64, 2, 2, 2 __VA_ARGS__);                                      \
-        }                                                                                    \
-    } while (0)
+    // The narrow tiles run with the same area as one row of four waves, so
+    // each code is expanded by one wave only: 64 x 128 in place of 128 x 64
+    // (512 x 4096 x 11008 with split k-tiles: 2-bit 40.6 -> 35.5 us, base-3
+    // 51.5 -> 39.9 us) and, for 2-bit and 1-bit, 32 x 128 in place of 64 x 64
+    // (256 x 4096 x 4096: 14.0 -> 13.5 us).
+#define BL_TILE_128x64(...) BL_GEMM_TILE(64, 128, 1, 4, 2 __VA_ARGS__)
 #define BL_TILE_64x64(...) BL_GEMM_TILE(32, 128, 1, 4, 2 __VA_ARGS__)
     // 256 x 128 tiles when they make several rounds, or one round that keeps
     // more than half of the 256 CUs busy (measured faster than two rounds of
@@ -719,18 +717,12 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     // exactly half, one round of 128 x 128 tiles is faster), and, except for
     // base-3 (whose weight decode the 256 tokens of a tile share), their last
     // row of tiles is at least three quarters full (384 tokens: 128-row tiles
-    // are faster). 2-bit and 1-bit take the same area as 128 x 256 tiles, one
-    // row of eight waves of 128 x 32, so that each code is expanded by one wave
-    // only (512 x 12288 x 4096: 36.9 -> 33.4 us); base-3's 160-code k-tile does
-    // not split evenly over 128 rows of eight waves.
+    // are faster). They run as 128 x 256 tiles of the same area, one row of
+    // eight waves of 128 x 32, so that each code is expanded by one wave only
+    // (512 x 12288 x 4096: 2-bit 36.9 -> 33.4 us, base-3 44.4 -> 37.3 us).
     const bool rows_fill = LAYOUT == kLayoutBase3 || M % 256 == 0 || M % 256 >= 192;
-    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256))) {
-        if constexpr (LAYOUT != kLayoutBase3) {
-            BL_GEMM_TILE(128, 256, 1, 8, 2);
-        } else {
-            BL_GEMM_TILE(256, 128, 2, 4, 2);
-        }
-    }
+    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)))
+        BL_GEMM_TILE(128, 256, 1, 8, 2);
     if (long_k) {
         if constexpr (LAYOUT != kLayoutBase3) {
             // at most half a round of 128 x 64 tiles: 64 x 64 tiles, also
@@ -746,7 +738,7 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     // 97.7 -> 78.5 us, 256 x 4096 x 6144: 31.1 -> 28.7 us; at 26 k-tiles,
     // K = 4096, the split was 1-3% slower)
     if (LAYOUT == kLayoutBase3 && t_small <= 128 && ktiles >= split_kt)
-        BL_GEMM_TILE(128, 64, 2, 2, 2, 2);
+        BL_TILE_128x64(, 2);
     // base-3, most of one round of 128 x 128 tiles: two groups split each
     // tile's k-tiles (768 x 4096 x 4096: 30.4 -> 29.0 us, 640 x 4096 x 4096:
     // 29.9 -> 28.9 us; under 160 tiles the split was slower)
