@@ -254,6 +254,8 @@ def test_forward_long_rows_sampled(bl, layout):
     ("2bit", 70000, 200, 256, "gemm_kernel<0, 128, 128, 1, 4, 2, 1, 0, unsigned short>"),
     ("1bit", 70000, 200, 256, "gemm_kernel<2, 128, 128, 1, 4, 2, 1, 0, unsigned short>"),
     ("base3", 70000, 200, 256, "gemm_kernel<1, 128, 256, 1, 8, 2, 1, 0, unsigned short>"),
+    # whole rounds of 256 x 256 tiles in the base-3 layout
+    ("base3", 4096, 4096, 4096, "gemm_kernel<1, 256, 256, 1, 8, 2, 1, 0, unsigned short>"),
 ])
 def test_forward_large_sampled(bl, layout, M, N, K, kernel):
     """Dispatch cases too large for a full oracle product: the configuration is
