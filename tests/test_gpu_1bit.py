@@ -87,8 +87,8 @@ FWD_CASES = [
     # long rows: two wave groups split the k-tiles (no padding: unguarded
     # whole tiles; padding: guarded)
     (140, 333, 8192), (140, 200, 9000),
-    # at most one round of 64 x 64 tiles over 32 k-tiles: split k-tiles on
-    # whole rows
+    # at most one round of 64 x 64 tiles over 32 k-tiles (launched as 32 x 128
+    # tiles of the same area): split k-tiles on whole rows
     (200, 1000, 4096),
 ]
 

@@ -158,7 +158,7 @@ FWD_CASES = [
     (17, 4096, 512), (96, 512, 4096), (40, 20000, 64), (33, 17000, 100), (31, 40000, 32),
     (64, 20000, 64), (120, 1000, 9000),
     # enough 256 x 256 tiles for a full round plus leftover columns (a second
-    # launch, or one paired launch when the leftover fills a round of 256 x 128)
+    # launch, or one paired launch when the leftover fills a round of 128 x 256)
     (4096, 4357, 64), (2048, 8200, 48), (2000, 11000, 48), (2048, 11008, 40),
     # many rows at M <= 4 (the four-wave weight-streaming launch shape)
     (2, 16400, 96), (1, 16384, 33),
@@ -170,20 +170,22 @@ FWD_CASES = [
     (130, 300, 9001), (200, 520, 8192), (130, 256, 10400), (150, 700, 12001), (97, 64, 16384),
     (130, 1900, 8192), (130, 2000, 10400),
     # 33 k-tiles over few tiles (2-bit at K = 4224, base-3 at K = 5280): two
-    # wave groups split them (2-bit 64 x 64 tiles, base-3 128 x 64)
+    # wave groups split them (2-bit 32 x 128 tiles, base-3 64 x 128)
     (256, 256, 4224), (256, 1100, 5280),
     # an odd number of k-tiles on whole tiles under one wave group: the last
-    # step runs alone, unguarded (2-bit 64 x 64 tiles, 3 k-tiles; base-3 takes
+    # step runs alone, unguarded (2-bit 32 x 128 tiles, 3 k-tiles; base-3 takes
     # its guarded path at K = 384)
     (300, 300, 384),
     # rows of K % 16 != 0 bytes but 4-byte aligned (dword loads), beside the
     # byte-wise odd K above
     (300, 700, 2052), (257, 1000, 4100),
     # base-3 with 160 to 256 tiles of 128 x 128: two groups split each tile's
-    # k-tiles (whole and ragged rows; 2-bit takes 64 x 64 tiles here)
+    # k-tiles (whole and ragged rows; 2-bit takes 32 x 128 tiles here)
     (1280, 2048, 160), (1200, 2000, 333),
     # long rows with at most half a round of 128 x 64 tiles: 2-bit takes
-    # 64 x 64 tiles with split k-tiles (edge tiles in both directions)
+    # 64 x 64 tiles with split k-tiles (edge tiles in both directions; the
+    # dispatch counts 128 x 64 and 64 x 64 tiles and launches 64 x 128 and
+    # 32 x 128 tiles of the same area)
     (250, 1000, 8200),
     # at most one round of 64 x 64 tiles (2-bit) or half a round of 128 x 64
     # tiles (base-3) over 32 or more k-tiles: split k-tiles at K = 4096, on
