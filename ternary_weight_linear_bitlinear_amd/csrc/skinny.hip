@@ -32,9 +32,22 @@ namespace {
 // with four loads keep more bytes in flight per CU and stream faster.
 // Batches at N >= 8192 put three (up to 12288 rows: one round of at most
 // 256 workgroups) or two row groups in a workgroup, cutting the activation
-// staging per weight byte.
+// staging per weight byte. A batch of one 16-token chunk with one or three
+// row groups, and one token over rows longer than a round with at most one
+// tile per CU, run sixteen waves with one load per lane: each wave's
+// expand-and-multiply chain after the weights land is half as long (2-bit
+// 16 x 4096 x 4096 4.6 -> 4.4 us, base-3 5.7 -> 5.2 us, base-3 16 x 12288 x
+// 4096 8.9 -> 8.5 us, one token over 4096 x 11008 8.9 -> 8.4 us); with two
+// row groups or several chunks they were slower (2-bit 16 x 16384 x 4096
+// 8.5 -> 9.6 us, 40 x 4096 x 4096 7.4 -> 8.2 us). One token over one-round
+// rows with more tiles than CUs runs four waves with four loads, which keep
+// more blocks resident (8192 x 4096 5.8 -> 4.7 us, 11008 x 4096 6.8 -> 6.0
+// us; at 4096 rows the same as eight waves).
 constexpr int kSkKS = 8, kSkNSS = 2, kSkRG2MinN = 8192;
 constexpr int kFdKS = 8, kFdNSS = 2;
+constexpr int kOneKS = 16, kOneNSS = 1;
+static_assert(kOneKS * kOneNSS == kFdKS * kFdNSS && kFdKS * kFdNSS == 4 * 4,
+              "every one-token launch shape covers 64 units per round");
 constexpr int64_t kWideN = 16384;
 
 // 16 elements of x held as raw 16-byte pieces (two for bf16, four for fp32),
@@ -446,12 +459,20 @@ hipError_t launch_skinny_l(const int8_t *xq, const float *scale, const uint8_t *
                                                                y, acc, s);
     // up to 16 x 256 x 3 rows: three row groups, so that one round of
     // workgroups (at most one per compute unit) covers the matrix
-    if (N >= kSkRG2MinN && N <= 16 * 256 * 3)
+    const bool one_chunk = M <= 16;  // larger batches run as several 16-token chunks
+    if (N >= kSkRG2MinN && N <= 16 * 256 * 3) {
+        if (one_chunk)
+            return launch_skinny_t<LAYOUT, kOneKS, kOneNSS, 3, 16, YT>(xq, scale, packed, gamma, M,
+                                                                     N, K, y, acc, s);
         return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 3, 16, YT>(xq, scale, packed, gamma, M, N, K,
                                                                y, acc, s);
+    }
     if (N >= kSkRG2MinN)
         return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 2, 16, YT>(xq, scale, packed, gamma, M, N, K,
                                                                y, acc, s);
+    if (one_chunk)
+        return launch_skinny_t<LAYOUT, kOneKS, kOneNSS, 1, 16, YT>(xq, scale, packed, gamma, M, N,
+                                                                 K, y, acc, s);
     return launch_skinny_t<LAYOUT, kSkKS, kSkNSS, 1, 16, YT>(xq, scale, packed, gamma, M, N, K,
                                                            y, acc, s);
 }
@@ -801,9 +822,20 @@ hipError_t launch_linear_t(const XT *x, const uint8_t *packed, const GammaMap &g
         return launch_linear_m<LAYOUT, 1, 4, 4, false, XT, YT, 2>(x, packed, gamma, M, N, K,
                                                                   (N + 31) / 32, y, acc, s);
     }
-    if (M == 1)
+    if (M == 1) {
+        // a round is 64 units for every launch shape below (KS * NSS = 16)
+        const bool one_round =
+            row_bytes_of(LAYOUT, K) / SkinnyCfg<LAYOUT>::kUnitBytes <= (int64_t)kFdKS * kFdNSS * 4;
+        const int64_t cus = device_cu_count();
+        if (one_round && cus > 0 && tiles > cus)
+            return launch_linear_m<LAYOUT, 1, 4, 4, false>(x, packed, gamma, M, N, K, tiles, y,
+                                                           acc, s);
+        if (!one_round && cus > 0 && tiles <= cus)
+            return launch_linear_m<LAYOUT, 1, kOneKS, kOneNSS, false>(x, packed, gamma, M, N, K,
+                                                                      tiles, y, acc, s);
         return launch_linear_m<LAYOUT, 1, kFdKS, kFdNSS, false>(x, packed, gamma, M, N, K, tiles,
                                                                 y, acc, s);
+    }
     return launch_linear_m<LAYOUT, kFusedMaxM, kFdKS, kFdNSS, false>(x, packed, gamma, M, N, K,
                                                                      tiles, y, acc, s);
 }

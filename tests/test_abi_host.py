@@ -234,9 +234,9 @@ def test_forward_plan_names_the_kernels(bl):
     assert plan[0].startswith("linear_decode_kernel<0, 8, 2, 1, false, 1, unsigned short, float> "
                               "grid=256x1 block=512")
     plan = bl.bitlinear_forward_plan(16, 12288, 4096, "2bit", torch.bfloat16)
-    assert plan[0].startswith("skinny_kernel<0, 8, 2, 3, 16, false, unsigned short> grid=256x1")
+    assert plan[0].startswith("skinny_kernel<0, 16, 1, 3, 16, false, unsigned short> grid=256x1")
     plan = bl.bitlinear_forward_plan(16, 4096, 11008, "2bit", torch.bfloat16)
-    assert plan[0].startswith("skinny_kernel<0, 8, 2, 1, 16, true, unsigned short> grid=256x1")
+    assert plan[0].startswith("skinny_kernel<0, 16, 1, 1, 16, true, unsigned short> grid=256x1")
     assert bl.bitlinear_forward_plan(0, 5, 5) == []
     with pytest.raises(bl.BitLinearError):
         bl.bitlinear_forward_plan(5, 4096, 4096, fused=True)

@@ -201,10 +201,10 @@ def block_inputs(M, K):
 
 
 BLOCK_16 = {
-    "qkv": "skinny_kernel<0, 8, 2, 3, 16, false, unsigned short>",
-    "o": "skinny_kernel<0, 8, 2, 1, 16, false, unsigned short>",
-    "up": "skinny_kernel<0, 8, 2, 3, 16, false, unsigned short>",
-    "down": "skinny_kernel<0, 8, 2, 1, 16, true, unsigned short>",
+    "qkv": "skinny_kernel<0, 16, 1, 3, 16, false, unsigned short>",
+    "o": "skinny_kernel<0, 16, 1, 1, 16, false, unsigned short>",
+    "up": "skinny_kernel<0, 16, 1, 3, 16, false, unsigned short>",
+    "down": "skinny_kernel<0, 16, 1, 1, 16, true, unsigned short>",
 }
 BLOCK_512 = {
     "qkv": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",

@@ -193,6 +193,10 @@ FWD_CASES = [
     (200, 1000, 4096), (192, 900, 5000), (200, 1000, 6000),
     # ragged rows split from 16 k-tiles on
     (200, 2000, 3000),
+    # one chunk of 5-16 tokens on sixteen waves of one load per lane: three
+    # row groups over rows longer than a round (2-bit) or one round (base-3),
+    # one row group over long ragged rows
+    (7, 9000, 4100), (9, 700, 9001),
 ]
 
 
@@ -400,7 +404,12 @@ def test_zero_activation_row_gives_zero_output(bl):
                                          # capped grid (two blocks per compute unit):
                                          # blocks stream tiles; ragged last tile
                                          (2, 8200, 64, "bf16"), (3, 12000, 4096, "f32"),
-                                         (4, 22016, 4096, "bf16"), (2, 9000, 5120, "bf16")])
+                                         (4, 22016, 4096, "bf16"), (2, 9000, 5120, "bf16"),
+                                         # one token: four waves of four loads over one-round
+                                         # rows with more tiles than CUs; sixteen waves of one
+                                         # load over longer rows with at most one tile per CU
+                                         (1, 11008, 4096, "bf16"), (1, 6000, 1000, "f32"),
+                                         (1, 300, 9001, "bf16"), (1, 4096, 8192, "f32")])
 def test_fused_linear_parity(bl, layout, M, N, K, dtype):
     """Same activation codes as the stand-alone quantiser (bit-exact), hence
     the same INT32 accumulators as the oracle, and y within tolerance."""
@@ -414,6 +423,18 @@ def test_fused_linear_parity(bl, layout, M, N, K, dtype):
     got = dict(packed=to_np(packed), gamma=to_np(gamma)[0], xq=ref["xq"], scale=ref["scale"],
                acc=to_np(acc), y=y)
     assert check_end_to_end(got, ref, p, layout, torch.float32) == 0
+
+
+@pytest.mark.parametrize("N,K,shape", [(11008, 4096, "4, 4"), (6000, 1000, "4, 4"),
+                                       (4096, 4096, "8, 2"), (4096, 8192, "16, 1"),
+                                       (300, 9001, "16, 1")])
+def test_fused_one_token_launch_shape(bl, N, K, shape):
+    """One token: the launch shape (waves, loads per lane) the parity cases
+    above reach, by the dispatch's dry run on this device."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the rule counts tiles against the compute units of an MI355X")
+    plan = bl.bitlinear_forward_plan(1, N, K, "2bit", torch.float32, fused=True)
+    assert plan[0].startswith(f"linear_decode_kernel<0, {shape}, 1, false, 1, "), plan
 
 
 def test_fused_linear_decode_full(bl):
