@@ -627,10 +627,10 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_kernel(const GemmArgs<
 
 // The prefill shape in one launch: the first blocks cover the columns that
 // fill whole rounds of 256 x 256 tiles, the rest the leftover columns in
-// 256 x 128 tiles. Leftover tiles start as soon as CUs free up, so their
-// start-up overlaps the output writes of the large tiles (and no second
-// launch is waited for).
-template <int LAYOUT, int KMODE, typename YT>
+// BM2 x 256 tiles (BM2 = 128, or 96 when those still make one round).
+// Leftover tiles start as soon as CUs free up, so their start-up overlaps the
+// output writes of the large tiles (and no second launch is waited for).
+template <int LAYOUT, int KMODE, typename YT, int BM2>
 __global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, int blocks1,
                                                         const GemmArgs<YT> g2) {
     const int b = blockIdx.x;
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(512) void gemm_pair_kernel(const GemmArgs<YT> g1, i
         if (t >= 0) gemm_tile<LAYOUT, 256, 256, 1, 8, 2, 1, KMODE, YT>(g1, t);
     } else {
         const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
-        if (t >= 0) gemm_tile<LAYOUT, 128, 256, 1, 8, 2, 1, KMODE, YT>(g2, t);
+        if (t >= 0) gemm_tile<LAYOUT, BM2, 256, 1, 8, 2, 1, KMODE, YT>(g2, t);
     }
 }
 
@@ -763,23 +763,23 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
 #undef BL_GEMM_TILE
 }
 
-// Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in 128 x 256 tiles,
+// Columns [0, n_main) in 256 x 256 tiles and [n_main, N) in BM2 x 256 tiles,
 // one launch.
-template <int LAYOUT, typename YT>
+template <int LAYOUT, int BM2, typename YT>
 hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t *packed,
                             const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t n_main,
                             YT *y, int32_t *acc, hipStream_t s) {
     using C1 = GemmCfg<LAYOUT, 256, 256, 1, 8, 2>;
-    using C2 = GemmCfg<LAYOUT, 128, 256, 1, 8, 2>;
+    using C2 = GemmCfg<LAYOUT, BM2, 256, 1, 8, 2>;
     static_assert(C1::SMEM >= C2::SMEM && C1::kThreads == C2::kThreads, "one launch shape");
     const int64_t rb = row_bytes_of(LAYOUT, K);
-    const int tm = (int)((M + 255) / 256), tm2 = (int)((M + 127) / 128);
+    const int tm = (int)((M + 255) / 256), tm2 = (int)((M + BM2 - 1) / BM2);
     const int tn1 = (int)((n_main + 255) / 256), tn2 = (int)((N - n_main + 255) / 256);
     GemmArgs<YT> g1{xq, scale, packed, gamma, M, n_main, K, rb, tm, tn1, y, N, acc};
     GemmArgs<YT> g2{xq, scale, packed + n_main * rb, gamma.from_row(n_main), M, N - n_main,
                     K, rb, tm2, tn2, y + n_main, N, acc ? acc + n_main : nullptr};
     g1.band = tile_band(tm, tn1, 256 * K, 256 * rb);
-    g2.band = tile_band(tm2, tn2, 128 * K, 256 * rb);
+    g2.band = tile_band(tm2, tn2, BM2 * K, 256 * rb);
     const int blocks1 = (tm * tn1 + kXcds - 1) / kXcds * kXcds;
     const int blocks2 = (tm2 * tn2 + kXcds - 1) / kXcds * kXcds;
     auto launch = [&](auto kern, LdsFlag *flag) {
@@ -791,15 +791,15 @@ hipError_t launch_gemm_pair(const int8_t *xq, const float *scale, const uint8_t 
     };
     if (t_plan) {
         plan_note((unsigned)(blocks1 + blocks2), 1, C1::kThreads, C1::SMEM,
-                  "gemm_pair_kernel<%d, %d, %s> (%d tiles 256x256 + %d tiles 128x256)", LAYOUT,
-                  gemm_k_mode(LAYOUT, K), type_name<YT>(), tm * tn1, tm2 * tn2);
+                  "gemm_pair_kernel<%d, %d, %s, %d> (%d tiles 256x256 + %d tiles %dx256)", LAYOUT,
+                  gemm_k_mode(LAYOUT, K), type_name<YT>(), BM2, tm * tn1, tm2 * tn2, BM2);
         return hipSuccess;
     }
     static LdsFlag lds_flag[3];  // one per k-mode
     switch (gemm_k_mode(LAYOUT, K)) {
-        case kWholeK: return launch(gemm_pair_kernel<LAYOUT, kWholeK, YT>, &lds_flag[0]);
-        case kGuardedK: return launch(gemm_pair_kernel<LAYOUT, kGuardedK, YT>, &lds_flag[1]);
-        default: return launch(gemm_pair_kernel<LAYOUT, kRaggedK, YT>, &lds_flag[2]);
+        case kWholeK: return launch(gemm_pair_kernel<LAYOUT, kWholeK, YT, BM2>, &lds_flag[0]);
+        case kGuardedK: return launch(gemm_pair_kernel<LAYOUT, kGuardedK, YT, BM2>, &lds_flag[1]);
+        default: return launch(gemm_pair_kernel<LAYOUT, kRaggedK, YT, BM2>, &lds_flag[2]);
     }
 }
 
@@ -824,9 +824,18 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
             const int64_t n_main = tn_main * 256 < N ? tn_main * 256 : N;
             const int64_t n_rest = N - n_main;
             const int64_t t_rest = ((M + 127) / 128) * ((n_rest + 255) / 256);
-            if (n_rest > 0 && t_rest >= 128 && t_rest <= kCUs)
-                return launch_gemm_pair<LAYOUT>(xq, scale, packed, gamma, M, N, K, n_main, y, acc,
-                                                s);
+            if (n_rest > 0 && t_rest >= 128 && t_rest <= kCUs) {
+                // 96-row leftover tiles when they still make one round: more
+                // CUs share the leftover work (prefill 2048 x 11008 x 4096:
+                // 176 tiles of 128 x 256 -> 242 of 96 x 256; 2-bit 94.9 ->
+                // 93.4 us, base-3 104.7 -> 101.0 us, 1-bit 93.9 -> 90.5 us)
+                const int64_t t_rest96 = ((M + 95) / 96) * ((n_rest + 255) / 256);
+                if (t_rest96 <= kCUs)
+                    return launch_gemm_pair<LAYOUT, 96>(xq, scale, packed, gamma, M, N, K, n_main,
+                                                        y, acc, s);
+                return launch_gemm_pair<LAYOUT, 128>(xq, scale, packed, gamma, M, N, K, n_main, y,
+                                                     acc, s);
+            }
             hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 1, 8, 2>(
                 xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
             if (e != hipSuccess || n_main == N) return e;

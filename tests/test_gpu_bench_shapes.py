@@ -184,9 +184,9 @@ def test_bench_weight_stream_32768(bl, layout):
 
 # --------------------------------------------------------------- prefill, C3
 @pytest.mark.parametrize("layout,kernel", [
-    ("2bit", "gemm_pair_kernel<0, 0, unsigned short> (256 tiles 256x256 + 176 tiles 128x256)"),
-    ("base3", "gemm_pair_kernel<1, 0, unsigned short> (256 tiles 256x256 + 176 tiles 128x256)"),
-    ("1bit", "gemm_pair_kernel<2, 0, unsigned short> (256 tiles 256x256 + 176 tiles 128x256)"),
+    ("2bit", "gemm_pair_kernel<0, 0, unsigned short, 96> (256 tiles 256x256 + 242 tiles 96x256)"),
+    ("base3", "gemm_pair_kernel<1, 0, unsigned short, 96> (256 tiles 256x256 + 242 tiles 96x256)"),
+    ("1bit", "gemm_pair_kernel<2, 0, unsigned short, 96> (256 tiles 256x256 + 242 tiles 96x256)"),
 ])
 def test_bench_prefill(bl, layout, kernel):
     p = synth.workload("prefill")

@@ -160,6 +160,7 @@ FWD_CASES = [
     # enough 256 x 256 tiles for a full round plus leftover columns (a second
     # launch, or one paired launch when the leftover fills a round of 128 x 256)
     (4096, 4357, 64), (2048, 8200, 48), (2000, 11000, 48), (2048, 11008, 40),
+    (2048, 11192, 48),
     # many rows at M <= 4 (the four-wave weight-streaming launch shape)
     (2, 16400, 96), (1, 16384, 33),
     # long rows (64 or more k-tiles) over few tiles: two wave groups split each
@@ -262,6 +263,16 @@ def test_forward_long_rows_sampled(bl, layout):
     ("base3", 70000, 200, 256, "gemm_kernel<1, 128, 256, 1, 8, 2, 1, 0, unsigned short>"),
     # whole rounds of 256 x 256 tiles in the base-3 layout
     ("base3", 4096, 4096, 4096, "gemm_kernel<1, 256, 256, 1, 8, 2, 1, 0, unsigned short>"),
+    # one launch of 256 x 256 tiles plus the leftover columns: 96-row leftover
+    # tiles where they make one round (ragged last row tile), else 128-row ones
+    ("2bit", 2000, 11000, 256,
+     "gemm_pair_kernel<0, 0, unsigned short, 96> (256 tiles 256x256 + 231 tiles 96x256)"),
+    ("base3", 2000, 11000, 200,
+     "gemm_pair_kernel<1, 2, unsigned short, 96> (256 tiles 256x256 + 231 tiles 96x256)"),
+    ("1bit", 2000, 11000, 256,
+     "gemm_pair_kernel<2, 0, unsigned short, 96> (256 tiles 256x256 + 231 tiles 96x256)"),
+    ("2bit", 2048, 11192, 256,
+     "gemm_pair_kernel<0, 0, unsigned short, 128> (256 tiles 256x256 + 192 tiles 128x256)"),
 ])
 def test_forward_large_sampled(bl, layout, M, N, K, kernel):
     """Dispatch cases too large for a full oracle product: the configuration is
