@@ -14,8 +14,9 @@ the step count.
 The same run measures the other rows of the path and reports them under
 "rows": the base-3 layout of the decode GEMV, weight packing, activation
 quantisation at prefill size, the prefill GEMM (M = 2048, K = 4096,
-N = 11008, INT8 TOPS), one transformer block's six BitLinear layers at
-decode batch 16 and prefill 512 (tokens/s), the training step at
+N = 11008, INT8 TOPS), one transformer block's six BitLinear layers for one
+decode token (four fused launches), at decode batch 16 and at prefill 512
+(tokens/s), the training step at
 M = K = N = 4096 (re-quantise, INT8 forward, bf16 straight-through backward
 products) and, for context, the same decode and prefill layers with dense
 bf16 weights through torch linear (hipBLASLt).
@@ -399,6 +400,32 @@ def main():
             qkv[s_ * 4096:(s_ + 1) * 4096].copy_(layers[s_][3])
             qkv_g[s_:s_ + 1].copy_(layers[s_][4])
         blk = {}
+        # one decode token through the block: four fused launches (quantise +
+        # multiply each), Q|K|V stacked; 16 rotating copies (629 MB of codes)
+        cps1 = [[(n, N, K, pk.clone() if c else pk, g) for (n, N, K, pk, g) in layers]
+                for c in range(16)]
+        qkvs1 = [qkv.clone() if c else qkv for c in range(16)]
+        x1 = {K: to_dev(synth.make_problem(M=1, N=1, K=K, seed=77 + K, dtype="bf16").x_store, True)
+              for K in (4096, 11008)}
+        ys1 = [torch.empty((1, N), dtype=torch.bfloat16, device=dev) for (_, N, _, _, _) in layers]
+        y1_qkv = torch.empty((1, 3 * 4096), dtype=torch.bfloat16, device=dev)
+
+        def block1(i):
+            c = i % len(cps1)
+            bl.bitlinear_linear_segmented(x1[4096], qkvs1[c], qkv_g, (4096, 4096, 4096), "2bit",
+                                          torch.bfloat16, y=y1_qkv)
+            for j in (3, 4, 5):
+                _, N, K, pk, g = cps1[c][j]
+                bl.bitlinear_linear(x1[K], pk, g, N, "2bit", torch.bfloat16, y=ys1[j])
+
+        ms = graph_ms(block1, 32)
+        blk["M1"] = dict(ms_per_block=ms, tokens_per_s=1 / (ms * 1e-3),
+                         weight_gbs=sum(l[3].numel() for l in layers) / (ms * 1e6),
+                         launches=4)
+        log(f"block M=1: {ms*1e3:.1f} us/block, four fused launches ({1/(ms*1e-3):.3g} tok/s, "
+            f"{blk['M1']['weight_gbs']:.0f} GB/s of codes)")
+        del cps1, qkvs1
+        torch.cuda.empty_cache()
         for M in (16, 512):
             ncopy = 16 if M == 16 else 1
             cps = [[(n, N, K, pk.clone() if c else pk, g) for (n, N, K, pk, g) in layers]

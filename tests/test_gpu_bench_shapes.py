@@ -9,7 +9,8 @@ compares the result with the oracle:
   layout) and the two-launch step (quantise, then the decode product);
 - one token against a 32768 x 4096 matrix (2-bit and 1-bit layouts);
 - prefill, 2048 x 11008 x 4096, bf16 out, all three layouts;
-- one transformer block's six projections at decode batch 16 and prefill 512:
+- one transformer block's six projections at one decode token (fused launches),
+  decode batch 16 and prefill 512:
   Q|K|V stacked as three segments with their own weight scales, O, up, down
   ([b158] §5.4 replaces exactly these linear layers with BitLinear);
 - the training shape's INT8 forward, 4096 x 4096 x 4096.
@@ -200,6 +201,12 @@ def block_inputs(M, K):
     return synth.make_problem(M=M, N=1, K=K, seed=77 + K, dtype="bf16")
 
 
+BLOCK_1 = {  # one token, fused quantise + multiply per launch
+    "qkv": "linear_decode_kernel<0, 4, 4, 1, false, 1, unsigned short, unsigned short>",
+    "o": "linear_decode_kernel<0, 8, 2, 1, false, 1, unsigned short, unsigned short>",
+    "up": "linear_decode_kernel<0, 4, 4, 1, false, 1, unsigned short, unsigned short>",
+    "down": "linear_decode_kernel<0, 16, 1, 1, false, 1, unsigned short, unsigned short>",
+}
 BLOCK_16 = {
     "qkv": "skinny_kernel<0, 16, 1, 3, 16, false, unsigned short>",
     "o": "skinny_kernel<0, 16, 1, 1, 16, false, unsigned short>",
@@ -214,18 +221,21 @@ BLOCK_512 = {
 }
 
 
-@pytest.mark.parametrize("M", [16, 512])
+@pytest.mark.parametrize("M", [1, 16, 512])
 @pytest.mark.parametrize("part", ["qkv", "o", "up", "down"])
 def test_bench_block(bl, M, part):
     """The block's launches as the benchmark makes them: Q|K|V as one stacked
     matrix of three segments with three weight scales, then O, up and down;
-    2-bit codes, bf16 out."""
+    2-bit codes, bf16 out. One token runs each as one fused launch (the launch
+    shape counts tiles against the compute units of an MI355X)."""
+    if M == 1 and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the one-token launch shape counts tiles against 256 compute units")
     idx = {"qkv": [0, 1, 2], "o": [3], "up": [4], "down": [5]}[part]
     ws = [synth.block_layer(i, 1) for i in idx]
     xp = block_inputs(M, ws[0].K)
-    kernel = (BLOCK_16 if M == 16 else BLOCK_512)[part]
-    rows = None if M == 16 else sample_rows(M, 8, 100 + idx[0])
-    check_case(bl, f"block M={M} {part}", ws, xp, "2bit", "ternary", torch.bfloat16, False,
+    kernel = {1: BLOCK_1, 16: BLOCK_16, 512: BLOCK_512}[M][part]
+    rows = None if M <= 16 else sample_rows(M, 8, 100 + idx[0])
+    check_case(bl, f"block M={M} {part}", ws, xp, "2bit", "ternary", torch.bfloat16, M == 1,
                kernel, rows=rows)
 
 
