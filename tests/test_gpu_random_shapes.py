@@ -93,6 +93,39 @@ def test_random_shape_parity(bl, case):
         check_y_bf16(to_np(y.view(torch.int16)).view(np.uint16)[~ex], ref["y64"][~ex])
 
 
+def draw_branch_cases(n, seed):
+    """Ragged shapes on the dispatch branches that pick a launch shape by size:
+    one token over more 16-row tiles than compute units (four waves, four loads
+    per lane) or over rows longer than a round (sixteen waves, one load), one
+    chunk of 5-16 tokens (sixteen waves; one or three row groups), and
+    prefill-like GEMMs with whole rounds of 256 x 256 tiles plus leftover
+    columns (96- or 128-row leftover tiles)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        layout = ["2bit", "base3", "1bit"][i % 3]
+        kind = i % 4
+        if kind == 0:
+            M, N, K = 1, int(rng.integers(4097, 16384)), int(rng.integers(16, 4200))
+        elif kind == 1:
+            M, N, K = 1, int(rng.integers(1, 4097)), int(rng.integers(4097, 14000))
+        elif kind == 2:
+            N = int(rng.integers(1, 8192)) if i % 8 == 2 else int(rng.integers(8192, 12289))
+            M, K = int(rng.integers(5, 17)), int(rng.integers(1, 9000))
+        else:
+            M, N, K = int(rng.integers(1800, 2300)), int(rng.integers(8300, 12300)), int(
+                rng.integers(16, 80))
+        cases.append((7000 + i, layout, M, N, K, ["f32", "bf16"][int(rng.integers(0, 2))],
+                      [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_branch_cases(24, 31),
+                         ids=lambda c: f"{c[1]}-M{c[2]}-N{c[3]}-K{c[4]}")
+def test_random_launch_shape_parity(bl, case):
+    test_random_shape_parity(bl, case)
+
+
 def draw_stacks(n, seed):
     rng = np.random.default_rng(seed)
     out = []
