@@ -827,8 +827,10 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
             if (n_rest > 0 && t_rest >= 128 && t_rest <= kCUs) {
                 // 96-row leftover tiles when they still make one round: more
                 // CUs share the leftover work (prefill 2048 x 11008 x 4096:
-                // 176 tiles of 128 x 256 -> 242 of 96 x 256; 2-bit 94.9 ->
-                // 93.4 us, base-3 104.7 -> 101.0 us, 1-bit 93.9 -> 90.5 us)
+                // 176 tiles of 128 x 256 -> 242 of 96 x 256; at steady clocks
+                // with flushed caches base-3 105.0 -> 101.6 us and 111.7 ->
+                // 109.4 us on two boxes, 1-bit 91.3 -> 91.3 and 100.7 -> 99.0
+                // us, 2-bit within 1% either way)
                 const int64_t t_rest96 = ((M + 95) / 96) * ((n_rest + 255) / 256);
                 if (t_rest96 <= kCUs)
                     return launch_gemm_pair<LAYOUT, 96>(xq, scale, packed, gamma, M, N, K, n_main,
