@@ -625,6 +625,221 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_kernel(const GemmArgs<
     gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, KG, KMODE, YT>(g, t);
 }
 
+// Whole 256 x 256 tiles of one matrix, 2-bit or 1-bit rows of whole k-tiles,
+// bf16 out: the activation tile reaches LDS by direct-to-LDS loads (16 bytes a
+// lane, no staging registers), three k-tiles deep, and the registers this
+// frees hold the next k-step's activation fragments while the current one is
+// multiplied. One row of eight waves as in gemm_tile, weights expanded in
+// registers the same way; the sums and outputs are identical.
+//
+// - Three static LDS arrays, one per stage. The compiler waits for every
+//   outstanding direct-to-LDS load before an LDS read that may alias it; reads
+//   of one array are not held up by loads into another.
+// - A wave's direct-to-LDS write is 1 KiB contiguous (lane l at 16 l), i.e.
+//   eight activation rows of 128 bytes with no padding. To keep the fragment
+//   reads free of bank conflicts, lane l loads chunk (l % 8) ^ ((row / 2) % 8)
+//   of its row, and readers look a chunk up at the same swizzled slot.
+// - Each step issues four direct-to-LDS loads and one weight load, after its
+//   first fragment reads and weight word. Before the step's barrier a wave
+//   waits until at most six vector-memory operations are outstanding: the
+//   weight load of the next k-tile and the five operations of this step. That
+//   leaves the next k-tile's own activation loads done, so the barrier
+//   publishes them to the other waves.
+// - The output tile leaves through a fourth array, 64 rows at a time.
+constexpr int kDmaStage = 256 * 128;  // one k-tile of activations, bytes
+constexpr int kDmaOutRow = 256 * 2 + 16;
+
+template <int LAYOUT, typename YT>
+__device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
+    static_assert(LAYOUT != kLayoutBase3 && sizeof(YT) == 2, "2-bit and 1-bit rows, bf16 out");
+    using C = GemmCfg<LAYOUT, 256, 256, 1, 8, 2>;
+    __shared__ __attribute__((aligned(16))) int8_t S0[kDmaStage];
+    __shared__ __attribute__((aligned(16))) int8_t S1[kDmaStage];
+    __shared__ __attribute__((aligned(16))) int8_t S2[kDmaStage];
+    __shared__ __attribute__((aligned(16))) uint8_t OUT[64 * kDmaOutRow];
+    const int8_t *__restrict__ xq = g.xq;
+    const float *__restrict__ scale = g.scale;
+    const int64_t K = g.K, rb = g.rb, ldy = g.ldy;
+    const int tiles_n = g.tiles_n;
+    YT *__restrict__ y = g.y;
+    int32_t *__restrict__ acc_out = g.acc_out;
+
+    int tr = t / tiles_n, tc = t % tiles_n;
+    if (g.band > 1) {
+        const int per_band = g.band * tiles_n;
+        const int b0 = t / per_band, idx = t - b0 * per_band;
+        const int rows = min(g.band, g.tiles_m - b0 * g.band);
+        tr = b0 * g.band + idx % rows;
+        tc = idx / rows;
+    }
+    const int64_t m0 = (int64_t)tr * 256, n0 = (int64_t)tc * 256;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int frow = lane % 32, lg = lane / 32;
+    const int64_t ktiles = rb / C::LB / 2;  // whole k-tiles (the caller checks)
+
+    // this lane's weight row and its four activation rows (wave w loads rows
+    // 32 w .. 32 w + 31, eight per instruction)
+    const uint8_t *bsrc = g.packed + (n0 + wave * 32 + frow) * rb;
+    const int8_t *asrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 32 * wave + 8 * j + lane / 8;
+        asrc[j] = xq + (m0 + row) * K + ((lane % 8) ^ ((row / 2) % 8)) * 16;
+    }
+    // k-tiles past the last re-read it (valid addresses; never multiplied)
+    auto load_a = [&](int64_t kt, int8_t *S) {
+        kt = kt < ktiles ? kt : ktiles - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(asrc[j] + kt * 128,
+                                             to_lds(S + (32 * wave + 8 * j) * 128), 16, 0, 0);
+    };
+    uint4 breg[3];
+    auto load_w = [&](int64_t kt, uint4 &r) {
+        kt = kt < ktiles ? kt : ktiles - 1;
+        r = load_b<LAYOUT>(bsrc + (kt * 2 + lg) * C::LB);
+    };
+
+    v16i acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0;
+
+    // fragment i, k-step ks of this lane: row 32 i + frow, chunk 4 lg + ks,
+    // at the swizzled slot ((row / 2) % 8 does not depend on i)
+    const int xs = (frow / 2) % 8;
+    auto frag = [&](const int8_t *S, int i, int ks) {
+        return *reinterpret_cast<const v4i *>(S + (i * 32 + frow) * 128 + ((4 * lg + ks) ^ xs) * 16);
+    };
+    auto expand = [&](const uint4 &bu, int ks, int (&c)[4]) {
+        if constexpr (LAYOUT == kLayout2Bit) {
+            expand_2bit_word(ks == 0 ? bu.x : ks == 1 ? bu.y : ks == 2 ? bu.z : bu.w, c);
+        } else {
+            expand_1bit_half(ks < 2 ? bu.x : bu.y, ks % 2, c);
+        }
+    };
+    // One k-tile from stage S; `issue` sends the loads of k-tile kt + 2 after
+    // the first fragment reads and weight word (see above).
+    auto step = [&](const int8_t *S, const uint4 &bu, auto issue) {
+        v4i a[2][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[0][i] = frag(S, i, 0);
+        int c0[4];
+        expand(bu, 0, c0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a[(ks + 1) & 1][i] = frag(S, i, ks + 1);
+            }
+            // keeps the next k-step's reads ahead of this k-step's multiplies
+            __builtin_amdgcn_sched_barrier(0);
+            int c[4] = {c0[0], c0[1], c0[2], c0[3]};
+            if (ks > 0) expand(bu, ks, c);
+            const v4i bj = v4i{c[0], c[1], c[2], c[3]};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bj, a[ks & 1][i], acc[i], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(6));
+        lds_barrier();
+    };
+
+    load_a(0, S0);
+    load_w(0, breg[0]);
+    load_a(1, S1);
+    load_w(1, breg[1]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(6));  // k-tile 0's activations
+    lds_barrier();
+    // k-tile kt sits in stage kt % 3 and weight set kt % 3
+    int64_t kt = 0;
+    for (; kt + 3 <= ktiles; kt += 3) {
+        step(S0, breg[0], [&]() { load_a(kt + 2, S2); load_w(kt + 2, breg[2]); });
+        step(S1, breg[1], [&]() { load_a(kt + 3, S0); load_w(kt + 3, breg[0]); });
+        step(S2, breg[2], [&]() { load_a(kt + 4, S1); load_w(kt + 4, breg[1]); });
+    }
+    if (kt < ktiles) step(S0, breg[0], [&]() { load_a(kt + 2, S2); load_w(kt + 2, breg[2]); });
+    if (kt + 1 < ktiles) step(S1, breg[1], [&]() { load_a(kt + 3, S0); load_w(kt + 3, breg[0]); });
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // no direct-to-LDS load outlives the block
+
+    // Epilogue: y = acc * gamma * scale[m] / 127 as bf16, rows 64 p .. 64 p + 63
+    // (fragments 2 p and 2 p + 1 of every wave) per pass
+    const float g0 = g.gm.g[0];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * p + ii;
+            const int64_t m = m0 + i * 32 + frow;
+            const float f1 = g0 * scale[m] / 127.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wave * 32 + 8 * q + 4 * lg;
+                const int32_t a0 = acc[i][4 * q], a1 = acc[i][4 * q + 1];
+                const int32_t a2 = acc[i][4 * q + 2], a3 = acc[i][4 * q + 3];
+                const bf16x2 lo = {(__bf16)((float)a0 * f1), (__bf16)((float)a1 * f1)};
+                const bf16x2 hi = {(__bf16)((float)a2 * f1), (__bf16)((float)a3 * f1)};
+                *reinterpret_cast<uint2 *>(OUT + (ii * 32 + frow) * kDmaOutRow + nl * 2) =
+                    make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                if (acc_out)
+                    *reinterpret_cast<int4 *>(acc_out + m * ldy + n0 + nl) = make_int4(a0, a1, a2, a3);
+            }
+        }
+        lds_barrier();
+        for (int c = tid; c < 64 * 32; c += 512) {  // 16-byte pieces of 64 output rows
+            const int row = c / 32, pc = c % 32;
+            const uint4 v = *reinterpret_cast<const uint4 *>(OUT + row * kDmaOutRow + pc * 16);
+            *reinterpret_cast<uint4 *>(y + (m0 + 64 * p + row) * ldy + n0 + pc * 8) = v;
+        }
+        lds_barrier();
+    }
+}
+
+template <int LAYOUT, typename YT>
+__global__ __launch_bounds__(512) void gemm_dma_kernel(const GemmArgs<YT> g) {
+    const int t = xcd_tile(blockIdx.x, g.tiles_m * g.tiles_n);
+    if (t < 0) return;
+    gemm_tile_dma<LAYOUT, YT>(g, t);
+}
+
+// The direct-to-LDS kernel serves a launch of 256 x 256 tiles when every tile is
+// whole (M and N multiples of 256), the rows hold whole k-tiles, the output is
+// bf16 with rows of whole 16-byte pieces, and one matrix is multiplied.
+template <int LAYOUT, typename YT>
+bool gemm_dma_fits(const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t ldy) {
+    if constexpr (LAYOUT == kLayoutBase3 || sizeof(YT) != 2) {
+        return false;
+    } else {
+        return M % 256 == 0 && N % 256 == 0 && ldy % 8 == 0 && gamma.nseg == 1 &&
+               gemm_k_mode(LAYOUT, K) == kWholeK;
+    }
+}
+
+template <int LAYOUT, typename YT>
+hipError_t launch_gemm_dma(const int8_t *xq, const float *scale, const uint8_t *packed,
+                           const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
+                           int64_t ldy, int32_t *acc, hipStream_t s) {
+    const int64_t rb = row_bytes_of(LAYOUT, K);
+    const int tm = (int)(M / 256), tn = (int)(N / 256);
+    GemmArgs<YT> g{xq, scale, packed, gamma, M, N, K, rb, tm, tn, y, ldy, acc};
+    g.band = tile_band(tm, tn, (int64_t)256 * K, (int64_t)256 * rb);
+    const unsigned blocks = (unsigned)((tm * tn + kXcds - 1) / kXcds * kXcds);
+    if (t_plan) {
+        // (static LDS: three stages and the output staging)
+        plan_note(blocks, 1, 512, 3 * kDmaStage + 64 * kDmaOutRow, "gemm_dma_kernel<%d, %s>",
+                  LAYOUT, type_name<YT>());
+        return hipSuccess;
+    }
+    if constexpr (LAYOUT != kLayoutBase3 && sizeof(YT) == 2)
+        hipLaunchKernelGGL((gemm_dma_kernel<LAYOUT, YT>), dim3(blocks), dim3(512), 0, s, g);
+    return hipGetLastError();
+}
+
 // The prefill shape in one launch: the first blocks cover the columns that
 // fill whole rounds of 256 x 256 tiles, the rest the leftover columns in
 // BM2 x 256 tiles (BM2 = 128, or 96 when those still make one round).
@@ -838,8 +1053,11 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
                 return launch_gemm_pair<LAYOUT, 128>(xq, scale, packed, gamma, M, N, K, n_main, y,
                                                      acc, s);
             }
-            hipError_t e = launch_gemm_tile<LAYOUT, 256, 256, 1, 8, 2>(
-                xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
+            hipError_t e = gemm_dma_fits<LAYOUT, YT>(gamma, M, n_main, K, N)
+                               ? launch_gemm_dma<LAYOUT>(xq, scale, packed, gamma, M, n_main, K,
+                                                         y, N, acc, s)
+                               : launch_gemm_tile<LAYOUT, 256, 256, 1, 8, 2>(
+                                     xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
             if (e != hipSuccess || n_main == N) return e;
             return launch_gemm_cols<LAYOUT>(xq, scale, packed + n_main * rb,
                                             gamma.from_row(n_main), M, N - n_main,

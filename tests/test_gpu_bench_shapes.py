@@ -245,5 +245,5 @@ def test_bench_train_forward(bl):
     256 x 256 tiles)."""
     t = synth.workload("train")
     check_case(bl, "train forward 4096^3", [t], t, "2bit", "ternary", torch.bfloat16, False,
-               "gemm_kernel<0, 256, 256, 1, 8, 2, 1, 0, unsigned short>", "256x1",
+               "gemm_dma_kernel<0, unsigned short>", "256x1",
                rows=sample_rows(t.M, 8, 5))

@@ -160,7 +160,7 @@ FWD_CASES = [
     # enough 256 x 256 tiles for a full round plus leftover columns (a second
     # launch, or one paired launch when the leftover fills a round of 128 x 256)
     (4096, 4357, 64), (2048, 8200, 48), (2000, 11000, 48), (2048, 11008, 40),
-    (2048, 11192, 48),
+    (2048, 11192, 48), (8192, 2048, 128),
     # many rows at M <= 4 (the four-wave weight-streaming launch shape)
     (2, 16400, 96), (1, 16384, 33),
     # long rows (64 or more k-tiles) over few tiles: two wave groups split each
@@ -273,6 +273,14 @@ def test_forward_long_rows_sampled(bl, layout):
      "gemm_pair_kernel<2, 0, unsigned short, 96> (256 tiles 256x256 + 231 tiles 96x256)"),
     ("2bit", 2048, 11192, 256,
      "gemm_pair_kernel<0, 0, unsigned short, 128> (256 tiles 256x256 + 192 tiles 128x256)"),
+    # whole 256 x 256 tiles, whole k-tiles, bf16 out: activations by direct-to-LDS
+    # loads through three stages (k-tile counts 1, 3 = one unrolled pass, 5 = a
+    # pass and both tail steps, 32; two rounds of tiles)
+    ("2bit", 8192, 2048, 128, "gemm_dma_kernel<0, unsigned short>"),
+    ("1bit", 4096, 4096, 384, "gemm_dma_kernel<2, unsigned short>"),
+    ("1bit", 8192, 2048, 640, "gemm_dma_kernel<2, unsigned short>"),
+    ("2bit", 4096, 4096, 4096, "gemm_dma_kernel<0, unsigned short>"),
+    ("2bit", 8192, 4096, 512, "gemm_dma_kernel<0, unsigned short>"),
 ])
 def test_forward_large_sampled(bl, layout, M, N, K, kernel):
     """Dispatch cases too large for a full oracle product: the configuration is
