@@ -625,41 +625,63 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_kernel(const GemmArgs<
     gemm_tile<LAYOUT, BM, BN, WM, WN, DIST, KG, KMODE, YT>(g, t);
 }
 
-// Whole 256 x 256 tiles of one matrix, 2-bit or 1-bit rows of whole k-tiles,
-// bf16 out: the activation tile reaches LDS by direct-to-LDS loads (16 bytes a
-// lane, no staging registers), three k-tiles deep, and the registers this
-// frees hold the next k-step's activation fragments while the current one is
-// multiplied. One row of eight waves as in gemm_tile, weights expanded in
-// registers the same way; the sums and outputs are identical.
+// BM x 256 tiles (BM = 256, 128 or 96) of 2-bit or 1-bit rows of whole k-tiles,
+// bf16 out, tiles whole in N: the activation tile reaches LDS by direct-to-LDS
+// loads (16 bytes a lane, no staging registers), three k-tiles deep, and the
+// registers this frees hold the next k-step's activation fragments while the
+// current one is multiplied. One row of eight waves as in gemm_tile (BM x 32
+// each), weights expanded in registers the same way; the sums are identical.
 //
-// - Three static LDS arrays, one per stage. The compiler waits for every
-//   outstanding direct-to-LDS load before an LDS read that may alias it; reads
-//   of one array are not held up by loads into another.
+// - Three LDS stages, each its own array (dma_lds). The compiler waits for
+//   every outstanding direct-to-LDS load before an LDS read that may alias it;
+//   reads of one array are not held up by loads into another. Every kernel
+//   that runs these tiles shares the same arrays (the one-launch pair runs two
+//   tile heights).
 // - A wave's direct-to-LDS write is 1 KiB contiguous (lane l at 16 l), i.e.
 //   eight activation rows of 128 bytes with no padding. To keep the fragment
 //   reads free of bank conflicts, lane l loads chunk (l % 8) ^ ((row / 2) % 8)
-//   of its row, and readers look a chunk up at the same swizzled slot.
-// - Each step issues four direct-to-LDS loads and one weight load, after its
-//   first fragment reads and weight word. Before the step's barrier a wave
-//   waits until at most six vector-memory operations are outstanding: the
-//   weight load of the next k-tile and the five operations of this step. That
-//   leaves the next k-tile's own activation loads done, so the barrier
-//   publishes them to the other waves.
+//   of its row, and readers look a chunk up at the same swizzled slot. Each
+//   wave loads 32 rows (BM = 256) or 16 rows (BM <= 128; for BM = 96 the
+//   last two waves load rows 96..127, which are never read). Rows past M
+//   re-read row M - 1 and feed only outputs that are not stored.
+// - Each step issues J direct-to-LDS loads and one weight load (J = 4 or 2),
+//   after its first fragment reads and weight word. Before the step's barrier
+//   a wave waits until at most J + 2 vector-memory operations are
+//   outstanding: the weight load of the next k-tile and the J + 1 operations
+//   of this step. That leaves the next k-tile's own activation loads done, so
+//   the barrier publishes them to the other waves.
 // - The output tile leaves through a fourth array, 64 rows at a time.
 constexpr int kDmaStage = 256 * 128;  // one k-tile of activations, bytes
 constexpr int kDmaOutRow = 256 * 2 + 16;
+struct DmaLds {
+    int8_t *s0, *s1, *s2;
+    uint8_t *out;
+};
+// The arrays of the stages and the output staging, declared once (not per tile
+// height) so that every kernel running these tiles shares them.
+__device__ __forceinline__ DmaLds dma_lds() {
+    __shared__ __attribute__((aligned(16))) int8_t s0[kDmaStage];
+    __shared__ __attribute__((aligned(16))) int8_t s1[kDmaStage];
+    __shared__ __attribute__((aligned(16))) int8_t s2[kDmaStage];
+    __shared__ __attribute__((aligned(16))) uint8_t out[64 * kDmaOutRow];
+    return DmaLds{s0, s1, s2, out};
+}
 
-template <int LAYOUT, typename YT>
+template <int LAYOUT, int BM, bool SEG, typename YT>
 __device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
     static_assert(LAYOUT != kLayoutBase3 && sizeof(YT) == 2, "2-bit and 1-bit rows, bf16 out");
-    using C = GemmCfg<LAYOUT, 256, 256, 1, 8, 2>;
-    __shared__ __attribute__((aligned(16))) int8_t S0[kDmaStage];
-    __shared__ __attribute__((aligned(16))) int8_t S1[kDmaStage];
-    __shared__ __attribute__((aligned(16))) int8_t S2[kDmaStage];
-    __shared__ __attribute__((aligned(16))) uint8_t OUT[64 * kDmaOutRow];
+    static_assert(BM == 256 || BM == 128 || BM == 96, "tile heights");
+    using C = GemmCfg<LAYOUT, BM, 256, 1, 8, 2>;
+    constexpr int FI = BM / 32;              // fragments per wave
+    constexpr int RPW = BM == 256 ? 32 : 16; // activation rows each wave loads
+    constexpr int J = RPW / 8;               // direct-to-LDS loads per wave and k-tile
+    const DmaLds lds = dma_lds();
+    int8_t *const dma_s0 = lds.s0, *const dma_s1 = lds.s1, *const dma_s2 = lds.s2;
+    uint8_t *const dma_out = lds.out;
     const int8_t *__restrict__ xq = g.xq;
     const float *__restrict__ scale = g.scale;
-    const int64_t K = g.K, rb = g.rb, ldy = g.ldy;
+    const GammaMap &gm = g.gm;
+    const int64_t M = g.M, K = g.K, rb = g.rb, ldy = g.ldy;
     const int tiles_n = g.tiles_n;
     YT *__restrict__ y = g.y;
     int32_t *__restrict__ acc_out = g.acc_out;
@@ -672,28 +694,30 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
         tr = b0 * g.band + idx % rows;
         tc = idx / rows;
     }
-    const int64_t m0 = (int64_t)tr * 256, n0 = (int64_t)tc * 256;
+    const int64_t m0 = (int64_t)tr * BM, n0 = (int64_t)tc * 256;
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int frow = lane % 32, lg = lane / 32;
     const int64_t ktiles = rb / C::LB / 2;  // whole k-tiles (the caller checks)
 
-    // this lane's weight row and its four activation rows (wave w loads rows
-    // 32 w .. 32 w + 31, eight per instruction)
+    // this lane's weight row and activation rows
     const uint8_t *bsrc = g.packed + (n0 + wave * 32 + frow) * rb;
+    // (sized for the largest J: an array sized by J would make the load builtin's
+    // arguments depend on BM, which the host compilation pass rejects)
     const int8_t *asrc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 32 * wave + 8 * j + lane / 8;
-        asrc[j] = xq + (m0 + row) * K + ((lane % 8) ^ ((row / 2) % 8)) * 16;
+    for (int j = 0; j < J; ++j) {
+        const int row = RPW * wave + 8 * j + lane / 8;
+        const int64_t m = m0 + row;
+        asrc[j] = xq + (m < M ? m : M - 1) * K + ((lane % 8) ^ ((row / 2) % 8)) * 16;
     }
     // k-tiles past the last re-read it (valid addresses; never multiplied)
     auto load_a = [&](int64_t kt, int8_t *S) {
         kt = kt < ktiles ? kt : ktiles - 1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < J; ++j)
             __builtin_amdgcn_global_load_lds(asrc[j] + kt * 128,
-                                             to_lds(S + (32 * wave + 8 * j) * 128), 16, 0, 0);
+                                             to_lds(S + (RPW * wave + 8 * j) * 128), 16, 0, 0);
     };
     uint4 breg[3];
     auto load_w = [&](int64_t kt, uint4 &r) {
@@ -701,9 +725,9 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
         r = load_b<LAYOUT>(bsrc + (kt * 2 + lg) * C::LB);
     };
 
-    v16i acc[8];
+    v16i acc[FI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0;
 
@@ -721,11 +745,12 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
         }
     };
     // One k-tile from stage S; `issue` sends the loads of k-tile kt + 2 after
-    // the first fragment reads and weight word (see above).
+    // the first fragment reads and weight word (a wait the compiler places
+    // before those then covers only loads of earlier steps).
     auto step = [&](const int8_t *S, const uint4 &bu, auto issue) {
-        v4i a[2][8];
+        v4i a[2][FI];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[0][i] = frag(S, i, 0);
+        for (int i = 0; i < FI; ++i) a[0][i] = frag(S, i, 0);
         int c0[4];
         expand(bu, 0, c0);
         __builtin_amdgcn_sched_barrier(0);
@@ -735,7 +760,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
         for (int ks = 0; ks < 4; ++ks) {
             if (ks + 1 < 4) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a[(ks + 1) & 1][i] = frag(S, i, ks + 1);
+                for (int i = 0; i < FI; ++i) a[(ks + 1) & 1][i] = frag(S, i, ks + 1);
             }
             // keeps the next k-step's reads ahead of this k-step's multiplies
             __builtin_amdgcn_sched_barrier(0);
@@ -743,100 +768,172 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs<YT> &g, int t) {
             if (ks > 0) expand(bu, ks, c);
             const v4i bj = v4i{c[0], c[1], c[2], c[3]};
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < FI; ++i)
                 acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bj, a[ks & 1][i], acc[i], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(6));
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(J + 2));
         lds_barrier();
     };
 
-    load_a(0, S0);
+    load_a(0, dma_s0);
     load_w(0, breg[0]);
-    load_a(1, S1);
+    load_a(1, dma_s1);
     load_w(1, breg[1]);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(6));  // k-tile 0's activations
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(J + 2));  // k-tile 0's activations
     lds_barrier();
     // k-tile kt sits in stage kt % 3 and weight set kt % 3
     int64_t kt = 0;
     for (; kt + 3 <= ktiles; kt += 3) {
-        step(S0, breg[0], [&]() { load_a(kt + 2, S2); load_w(kt + 2, breg[2]); });
-        step(S1, breg[1], [&]() { load_a(kt + 3, S0); load_w(kt + 3, breg[0]); });
-        step(S2, breg[2], [&]() { load_a(kt + 4, S1); load_w(kt + 4, breg[1]); });
+        step(dma_s0, breg[0], [&]() { load_a(kt + 2, dma_s2); load_w(kt + 2, breg[2]); });
+        step(dma_s1, breg[1], [&]() { load_a(kt + 3, dma_s0); load_w(kt + 3, breg[0]); });
+        step(dma_s2, breg[2], [&]() { load_a(kt + 4, dma_s1); load_w(kt + 4, breg[1]); });
     }
-    if (kt < ktiles) step(S0, breg[0], [&]() { load_a(kt + 2, S2); load_w(kt + 2, breg[2]); });
-    if (kt + 1 < ktiles) step(S1, breg[1], [&]() { load_a(kt + 3, S0); load_w(kt + 3, breg[0]); });
+    if (kt < ktiles)
+        step(dma_s0, breg[0], [&]() { load_a(kt + 2, dma_s2); load_w(kt + 2, breg[2]); });
+    if (kt + 1 < ktiles)
+        step(dma_s1, breg[1], [&]() { load_a(kt + 3, dma_s0); load_w(kt + 3, breg[0]); });
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // no direct-to-LDS load outlives the block
 
-    // Epilogue: y = acc * gamma * scale[m] / 127 as bf16, rows 64 p .. 64 p + 63
-    // (fragments 2 p and 2 p + 1 of every wave) per pass
-    const float g0 = g.gm.g[0];
+    // Epilogue: y = acc * f as bf16; one matrix: f = gamma * scale[m] / 127;
+    // stacked segments (SEG): f = gamma(n) * (scale[m] / 127). Rows 64 p ..
+    // 64 p + 63 (fragments 2 p and 2 p + 1 of every wave) per pass. (A single
+    // matrix has its own instantiation: the segment selection's registers
+    // cost the main loop 2-3% at 4096^3.)
+    float gs[SEG ? kMaxSegments : 1];
+    if constexpr (SEG) load_gammas(gm, gs);
+    else gs[0] = gm.g[0];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < (FI + 1) / 2; ++p) {
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             const int i = 2 * p + ii;
+            if (i >= FI) break;
             const int64_t m = m0 + i * 32 + frow;
-            const float f1 = g0 * scale[m] / 127.0f;
+            const float sm = scale[m < M ? m : M - 1];
+            const float f1 = gs[0] * sm / 127.0f;
+            const float sm127 = sm / 127.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int nl = wave * 32 + 8 * q + 4 * lg;
                 const int32_t a0 = acc[i][4 * q], a1 = acc[i][4 * q + 1];
                 const int32_t a2 = acc[i][4 * q + 2], a3 = acc[i][4 * q + 3];
-                const bf16x2 lo = {(__bf16)((float)a0 * f1), (__bf16)((float)a1 * f1)};
-                const bf16x2 hi = {(__bf16)((float)a2 * f1), (__bf16)((float)a3 * f1)};
-                *reinterpret_cast<uint2 *>(OUT + (ii * 32 + frow) * kDmaOutRow + nl * 2) =
+                float f[4] = {f1, f1, f1, f1};
+                if constexpr (SEG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) f[e] = seg_gamma(gm, gs, n0 + nl + e) * sm127;
+                }
+                const bf16x2 lo = {(__bf16)((float)a0 * f[0]), (__bf16)((float)a1 * f[1])};
+                const bf16x2 hi = {(__bf16)((float)a2 * f[2]), (__bf16)((float)a3 * f[3])};
+                *reinterpret_cast<uint2 *>(dma_out + (ii * 32 + frow) * kDmaOutRow + nl * 2) =
                     make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-                if (acc_out)
+                if (acc_out && m < M)
                     *reinterpret_cast<int4 *>(acc_out + m * ldy + n0 + nl) = make_int4(a0, a1, a2, a3);
             }
         }
         lds_barrier();
-        for (int c = tid; c < 64 * 32; c += 512) {  // 16-byte pieces of 64 output rows
+        const int rows = FI - 2 * p >= 2 ? 64 : 32;
+        for (int c = tid; c < rows * 32; c += 512) {  // 16-byte pieces of the pass's rows
             const int row = c / 32, pc = c % 32;
-            const uint4 v = *reinterpret_cast<const uint4 *>(OUT + row * kDmaOutRow + pc * 16);
-            *reinterpret_cast<uint4 *>(y + (m0 + 64 * p + row) * ldy + n0 + pc * 8) = v;
+            const int64_t m = m0 + 64 * p + row;
+            if (m < M) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(dma_out + row * kDmaOutRow + pc * 16);
+                *reinterpret_cast<uint4 *>(y + m * ldy + n0 + pc * 8) = v;
+            }
         }
         lds_barrier();
     }
 }
 
-template <int LAYOUT, typename YT>
+template <int LAYOUT, int BM, bool SEG, typename YT>
 __global__ __launch_bounds__(512) void gemm_dma_kernel(const GemmArgs<YT> g) {
     const int t = xcd_tile(blockIdx.x, g.tiles_m * g.tiles_n);
     if (t < 0) return;
-    gemm_tile_dma<LAYOUT, YT>(g, t);
+    gemm_tile_dma<LAYOUT, BM, SEG, YT>(g, t);
 }
 
-// The direct-to-LDS kernel serves a launch of 256 x 256 tiles when every tile is
-// whole (M and N multiples of 256), the rows hold whole k-tiles, the output is
-// bf16 with rows of whole 16-byte pieces, and one matrix is multiplied.
-template <int LAYOUT, typename YT>
-bool gemm_dma_fits(const GammaMap &gamma, int64_t M, int64_t N, int64_t K, int64_t ldy) {
-    if constexpr (LAYOUT == kLayoutBase3 || sizeof(YT) != 2) {
-        return false;
+// The prefill shape in one launch with the direct-to-LDS tiles: 256 x 256
+// tiles over whole rounds, then BM2 x 256 tiles over the leftover columns.
+template <int LAYOUT, int BM2, bool SEG, typename YT>
+__global__ __launch_bounds__(512) void gemm_dma_pair_kernel(const GemmArgs<YT> g1, int blocks1,
+                                                            const GemmArgs<YT> g2) {
+    const int b = blockIdx.x;
+    if (b < blocks1) {
+        const int t = xcd_tile(b, g1.tiles_m * g1.tiles_n);
+        if (t >= 0) gemm_tile_dma<LAYOUT, 256, SEG, YT>(g1, t);
     } else {
-        return M % 256 == 0 && N % 256 == 0 && ldy % 8 == 0 && gamma.nseg == 1 &&
-               gemm_k_mode(LAYOUT, K) == kWholeK;
+        const int t = xcd_tile(b - blocks1, g2.tiles_m * g2.tiles_n);
+        if (t >= 0) gemm_tile_dma<LAYOUT, BM2, SEG, YT>(g2, t);
     }
 }
 
+// The direct-to-LDS tiles serve a launch when its columns are whole 256-wide
+// tiles, the rows hold whole k-tiles (2-bit, or 1-bit without padding codes)
+// and the output is bf16 with rows of whole 16-byte pieces.
 template <int LAYOUT, typename YT>
+bool gemm_dma_fits(int64_t N, int64_t K, int64_t ldy) {
+    if constexpr (LAYOUT == kLayoutBase3 || sizeof(YT) != 2) {
+        return false;
+    } else {
+        return N % 256 == 0 && ldy % 8 == 0 && gemm_k_mode(LAYOUT, K) == kWholeK;
+    }
+}
+
+template <int LAYOUT, int BM, typename YT>
 hipError_t launch_gemm_dma(const int8_t *xq, const float *scale, const uint8_t *packed,
                            const GammaMap &gamma, int64_t M, int64_t N, int64_t K, YT *y,
                            int64_t ldy, int32_t *acc, hipStream_t s) {
     const int64_t rb = row_bytes_of(LAYOUT, K);
-    const int tm = (int)(M / 256), tn = (int)(N / 256);
+    const int tm = (int)((M + BM - 1) / BM), tn = (int)(N / 256);
     GemmArgs<YT> g{xq, scale, packed, gamma, M, N, K, rb, tm, tn, y, ldy, acc};
-    g.band = tile_band(tm, tn, (int64_t)256 * K, (int64_t)256 * rb);
+    g.band = tile_band(tm, tn, (int64_t)BM * K, (int64_t)256 * rb);
     const unsigned blocks = (unsigned)((tm * tn + kXcds - 1) / kXcds * kXcds);
     if (t_plan) {
         // (static LDS: three stages and the output staging)
-        plan_note(blocks, 1, 512, 3 * kDmaStage + 64 * kDmaOutRow, "gemm_dma_kernel<%d, %s>",
-                  LAYOUT, type_name<YT>());
+        plan_note(blocks, 1, 512, 3 * kDmaStage + 64 * kDmaOutRow,
+                  "gemm_dma_kernel<%d, %d, %s, %s>", LAYOUT, BM,
+                  gamma.nseg > 1 ? "true" : "false", type_name<YT>());
         return hipSuccess;
     }
     if constexpr (LAYOUT != kLayoutBase3 && sizeof(YT) == 2)
-        hipLaunchKernelGGL((gemm_dma_kernel<LAYOUT, YT>), dim3(blocks), dim3(512), 0, s, g);
+        if (gamma.nseg > 1)
+            hipLaunchKernelGGL((gemm_dma_kernel<LAYOUT, BM, true, YT>), dim3(blocks), dim3(512), 0,
+                               s, g);
+        else
+            hipLaunchKernelGGL((gemm_dma_kernel<LAYOUT, BM, false, YT>), dim3(blocks), dim3(512), 0,
+                               s, g);
+    return hipGetLastError();
+}
+
+template <int LAYOUT, int BM2, typename YT>
+hipError_t launch_gemm_dma_pair(const int8_t *xq, const float *scale, const uint8_t *packed,
+                                const GammaMap &gamma, int64_t M, int64_t N, int64_t K,
+                                int64_t n_main, YT *y, int32_t *acc, hipStream_t s) {
+    const int64_t rb = row_bytes_of(LAYOUT, K);
+    const int tm = (int)((M + 255) / 256), tm2 = (int)((M + BM2 - 1) / BM2);
+    const int tn1 = (int)(n_main / 256), tn2 = (int)((N - n_main) / 256);
+    GemmArgs<YT> g1{xq, scale, packed, gamma, M, n_main, K, rb, tm, tn1, y, N, acc};
+    GemmArgs<YT> g2{xq, scale, packed + n_main * rb, gamma.from_row(n_main), M, N - n_main,
+                    K, rb, tm2, tn2, y + n_main, N, acc ? acc + n_main : nullptr};
+    g1.band = tile_band(tm, tn1, 256 * K, 256 * rb);
+    g2.band = tile_band(tm2, tn2, BM2 * K, 256 * rb);
+    const int blocks1 = (tm * tn1 + kXcds - 1) / kXcds * kXcds;
+    const int blocks2 = (tm2 * tn2 + kXcds - 1) / kXcds * kXcds;
+    if (t_plan) {
+        plan_note((unsigned)(blocks1 + blocks2), 1, 512, 3 * kDmaStage + 64 * kDmaOutRow,
+                  "gemm_dma_pair_kernel<%d, %d, %s, %s> (%d tiles 256x256 + %d tiles %dx256)",
+                  LAYOUT, BM2, gamma.nseg > 1 ? "true" : "false", type_name<YT>(), tm * tn1,
+                  tm2 * tn2, BM2);
+        return hipSuccess;
+    }
+    if constexpr (LAYOUT != kLayoutBase3 && sizeof(YT) == 2) {
+        const dim3 grid((unsigned)(blocks1 + blocks2));
+        if (gamma.nseg > 1)
+            hipLaunchKernelGGL((gemm_dma_pair_kernel<LAYOUT, BM2, true, YT>), grid, dim3(512), 0, s,
+                               g1, blocks1, g2);
+        else
+            hipLaunchKernelGGL((gemm_dma_pair_kernel<LAYOUT, BM2, false, YT>), grid, dim3(512), 0,
+                               s, g1, blocks1, g2);
+    }
     return hipGetLastError();
 }
 
@@ -936,8 +1033,11 @@ hipError_t launch_gemm_cols(const int8_t *xq, const float *scale, const uint8_t 
     // eight waves of 128 x 32, so that each code is expanded by one wave only
     // (512 x 12288 x 4096: 2-bit 36.9 -> 33.4 us, base-3 44.4 -> 37.3 us).
     const bool rows_fill = LAYOUT == kLayoutBase3 || M % 256 == 0 || M % 256 >= 192;
-    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256)))
+    if (rows_fill && (t_wide >= 512 || (t_wide > 128 && t_wide <= 256))) {
+        if (gemm_dma_fits<LAYOUT, YT>(N, K, ldy))
+            return launch_gemm_dma<LAYOUT, 128>(xq, scale, packed, gamma, M, N, K, y, ldy, acc, s);
         BL_GEMM_TILE(128, 256, 1, 8, 2);
+    }
     if (long_k) {
         if constexpr (LAYOUT != kLayoutBase3) {
             // at most half a round of 128 x 64 tiles: 64 x 64 tiles, also
@@ -1047,15 +1147,20 @@ hipError_t launch_gemm_t(const int8_t *xq, const float *scale, const uint8_t *pa
                 // 109.4 us on two boxes, 1-bit 91.3 -> 91.3 and 100.7 -> 99.0
                 // us, 2-bit within 1% either way)
                 const int64_t t_rest96 = ((M + 95) / 96) * ((n_rest + 255) / 256);
+                const bool dma = gemm_dma_fits<LAYOUT, YT>(N, K, N);
                 if (t_rest96 <= kCUs)
-                    return launch_gemm_pair<LAYOUT, 96>(xq, scale, packed, gamma, M, N, K, n_main,
-                                                        y, acc, s);
-                return launch_gemm_pair<LAYOUT, 128>(xq, scale, packed, gamma, M, N, K, n_main, y,
-                                                     acc, s);
+                    return dma ? launch_gemm_dma_pair<LAYOUT, 96>(xq, scale, packed, gamma, M, N,
+                                                                  K, n_main, y, acc, s)
+                               : launch_gemm_pair<LAYOUT, 96>(xq, scale, packed, gamma, M, N, K,
+                                                              n_main, y, acc, s);
+                return dma ? launch_gemm_dma_pair<LAYOUT, 128>(xq, scale, packed, gamma, M, N, K,
+                                                               n_main, y, acc, s)
+                           : launch_gemm_pair<LAYOUT, 128>(xq, scale, packed, gamma, M, N, K,
+                                                           n_main, y, acc, s);
             }
-            hipError_t e = gemm_dma_fits<LAYOUT, YT>(gamma, M, n_main, K, N)
-                               ? launch_gemm_dma<LAYOUT>(xq, scale, packed, gamma, M, n_main, K,
-                                                         y, N, acc, s)
+            hipError_t e = gemm_dma_fits<LAYOUT, YT>(n_main, K, N)
+                               ? launch_gemm_dma<LAYOUT, 256>(xq, scale, packed, gamma, M, n_main,
+                                                              K, y, N, acc, s)
                                : launch_gemm_tile<LAYOUT, 256, 256, 1, 8, 2>(
                                      xq, scale, packed, gamma, M, n_main, K, y, N, acc, s);
             if (e != hipSuccess || n_main == N) return e;

@@ -225,10 +225,10 @@ def test_forward_plan_names_the_kernels(bl):
     shapes whose launch shape does not depend on the compute-unit count."""
     import torch
     plan = bl.bitlinear_forward_plan(2048, 11008, 4096, "2bit", torch.bfloat16)
-    assert len(plan) == 1 and plan[0].startswith("gemm_pair_kernel<0, 0, unsigned short, 96>")
+    assert len(plan) == 1 and plan[0].startswith("gemm_dma_pair_kernel<0, 96, false, unsigned short>")
     assert "(256 tiles 256x256 + 242 tiles 96x256)" in plan[0]
     plan = bl.bitlinear_forward_plan(4096, 4096, 4096, "2bit", torch.bfloat16)
-    assert plan == ["gemm_dma_kernel<0, unsigned short> grid=256x1 block=512 lds=132096"]
+    assert plan == ["gemm_dma_kernel<0, 256, false, unsigned short> grid=256x1 block=512 lds=132096"]
     plan = bl.bitlinear_forward_plan(4096, 4096, 4096, "base3", torch.bfloat16)
     assert plan == ["gemm_kernel<1, 256, 256, 1, 8, 2, 1, 0, unsigned short> grid=256x1 "
                     "block=512 lds=" + plan[0].split("lds=")[1]]

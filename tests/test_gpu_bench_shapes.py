@@ -185,9 +185,9 @@ def test_bench_weight_stream_32768(bl, layout):
 
 # --------------------------------------------------------------- prefill, C3
 @pytest.mark.parametrize("layout,kernel", [
-    ("2bit", "gemm_pair_kernel<0, 0, unsigned short, 96> (256 tiles 256x256 + 242 tiles 96x256)"),
+    ("2bit", "gemm_dma_pair_kernel<0, 96, false, unsigned short> (256 tiles 256x256 + 242 tiles 96x256)"),
     ("base3", "gemm_pair_kernel<1, 0, unsigned short, 96> (256 tiles 256x256 + 242 tiles 96x256)"),
-    ("1bit", "gemm_pair_kernel<2, 0, unsigned short, 96> (256 tiles 256x256 + 242 tiles 96x256)"),
+    ("1bit", "gemm_dma_pair_kernel<2, 96, false, unsigned short> (256 tiles 256x256 + 242 tiles 96x256)"),
 ])
 def test_bench_prefill(bl, layout, kernel):
     p = synth.workload("prefill")
@@ -214,9 +214,11 @@ BLOCK_16 = {
     "down": "skinny_kernel<0, 16, 1, 1, 16, true, unsigned short>",
 }
 BLOCK_512 = {
-    "qkv": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",
+    # (the dry run takes no segments: the stacked Q|K|V launch runs the same
+    # tiles in the instantiation that picks each row's weight scale, "true")
+    "qkv": "gemm_dma_kernel<0, 128, false, unsigned short>",
     "o": "gemm_kernel<0, 32, 128, 1, 4, 2, 1, 0, unsigned short>",
-    "up": "gemm_kernel<0, 128, 256, 1, 8, 2, 1, 0, unsigned short>",
+    "up": "gemm_dma_kernel<0, 128, false, unsigned short>",
     "down": "gemm_kernel<0, 64, 128, 1, 4, 2, 2, 0, unsigned short>",
 }
 
@@ -245,5 +247,5 @@ def test_bench_train_forward(bl):
     256 x 256 tiles)."""
     t = synth.workload("train")
     check_case(bl, "train forward 4096^3", [t], t, "2bit", "ternary", torch.bfloat16, False,
-               "gemm_dma_kernel<0, unsigned short>", "256x1",
+               "gemm_dma_kernel<0, 256, false, unsigned short>", "256x1",
                rows=sample_rows(t.M, 8, 5))

@@ -276,11 +276,18 @@ def test_forward_long_rows_sampled(bl, layout):
     # whole 256 x 256 tiles, whole k-tiles, bf16 out: activations by direct-to-LDS
     # loads through three stages (k-tile counts 1, 3 = one unrolled pass, 5 = a
     # pass and both tail steps, 32; two rounds of tiles)
-    ("2bit", 8192, 2048, 128, "gemm_dma_kernel<0, unsigned short>"),
-    ("1bit", 4096, 4096, 384, "gemm_dma_kernel<2, unsigned short>"),
-    ("1bit", 8192, 2048, 640, "gemm_dma_kernel<2, unsigned short>"),
-    ("2bit", 4096, 4096, 4096, "gemm_dma_kernel<0, unsigned short>"),
-    ("2bit", 8192, 4096, 512, "gemm_dma_kernel<0, unsigned short>"),
+    ("2bit", 8192, 2048, 128, "gemm_dma_kernel<0, 256, false, unsigned short>"),
+    ("1bit", 4096, 4096, 384, "gemm_dma_kernel<2, 256, false, unsigned short>"),
+    ("1bit", 8192, 2048, 640, "gemm_dma_kernel<2, 256, false, unsigned short>"),
+    ("2bit", 4096, 4096, 4096, "gemm_dma_kernel<0, 256, false, unsigned short>"),
+    ("2bit", 8192, 4096, 512, "gemm_dma_kernel<0, 256, false, unsigned short>"),
+    # the same tiles with ragged token rows: the one-launch pair with 96-row
+    # leftover tiles (2-bit) and 128-row ones (1-bit), and 128 x 256 tiles
+    ("2bit", 2000, 11008, 256,
+     "gemm_dma_pair_kernel<0, 96, false, unsigned short> (256 tiles 256x256 + 231 tiles 96x256)"),
+    ("1bit", 2040, 11264, 128,
+     "gemm_dma_pair_kernel<2, 128, false, unsigned short> (256 tiles 256x256 + 192 tiles 128x256)"),
+    ("2bit", 500, 12288, 256, "gemm_dma_kernel<0, 128, false, unsigned short>"),
 ])
 def test_forward_large_sampled(bl, layout, M, N, K, kernel):
     """Dispatch cases too large for a full oracle product: the configuration is
