@@ -126,6 +126,29 @@ def test_random_launch_shape_parity(bl, case):
     test_random_shape_parity(bl, case)
 
 
+def draw_lds_tile_cases(n, seed):
+    """Ragged token rows on the GEMM tiles that take activations by
+    direct-to-LDS loads: columns in whole 256-wide tiles, whole k-tiles (2-bit,
+    and 1-bit without padding codes), bf16 out; enough tiles for 256 x 256
+    rounds, the one-launch pair and 128 x 256 tiles."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        layout = ["2bit", "1bit"][i % 2]
+        M = int(rng.integers(380, 2300))
+        N = 256 * int(rng.integers(24, 48))
+        K = 128 * int(rng.integers(1, 4))
+        cases.append((8000 + i, layout, M, N, K, ["f32", "bf16"][int(rng.integers(0, 2))],
+                      torch.bfloat16))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_lds_tile_cases(12, 41),
+                         ids=lambda c: f"{c[1]}-M{c[2]}-N{c[3]}-K{c[4]}")
+def test_random_lds_tile_parity(bl, case):
+    test_random_shape_parity(bl, case)
+
+
 def draw_stacks(n, seed):
     rng = np.random.default_rng(seed)
     out = []
